@@ -1,0 +1,94 @@
+"""The pins catch plausible oracle mistakes.
+
+Each case plants one mistake in the oracle (on the CPU, via monkeypatch) and
+checks that at least one pin then fails.  This is evidence that the pins are
+sensitive, not only that the current oracle passes them.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as OA
+from oracle import ratios as OR
+from oracle import xa as OX
+import test_oracle_attention as TA
+import test_oracle_ratios as TR
+import test_oracle_xa as TX
+
+
+def _window_inclusive(mode, i_idx, j_idx, L, sink, window, block=None, xa_mask=None):
+    i = np.asarray(i_idx)[:, None]
+    j = np.asarray(j_idx)[None, :]
+    ok = (j <= i) & (j < L) & (i < L)
+    if mode == OA.MODE_SSA:
+        return ok & ((j < sink) | (i - j <= window))     # planted: <= instead of <
+    return _orig_allowed(mode, i_idx, j_idx, L, sink, window, block, xa_mask)
+
+
+_orig_allowed = OA.allowed_matrix
+
+
+def test_mutant_window_off_by_one(monkeypatch):
+    monkeypatch.setattr(OA, "allowed_matrix", _window_inclusive)
+    with pytest.raises(AssertionError):
+        TA.test_ssa_zero_query_closed_form(97, 5, 17)
+
+
+def test_mutant_dropped_scale(monkeypatch):
+    orig = OA.head_attention
+
+    def no_scale(qh, kh, vh, mode, scale, *a, **kw):
+        return orig(qh, kh, vh, mode, 1.0, *a, **kw)      # planted: scale dropped
+    monkeypatch.setattr(OA, "head_attention", no_scale)
+    with pytest.raises(AssertionError):
+        TA.test_fa_matches_textbook_sdpa()
+
+
+def test_mutant_main_diagonal_instead_of_antidiagonal(monkeypatch):
+    def reduced_no_reverse(qh, kg, S):
+        L, d = qh.shape
+        n = L // S
+        return qh.reshape(n, S * d), kg.reshape(n, S * d)   # planted: k not reversed
+    monkeypatch.setattr(OX, "_reduced", reduced_no_reverse)
+    with pytest.raises(AssertionError):
+        TX.test_antidiagonal_bruteforce(64, 16, 4, 5)
+
+
+def test_mutant_tie_break_descending(monkeypatch):
+    orig = OX.select_row
+
+    def desc_ties(P_row, I, tn, td):
+        # planted: equal weights ordered by J descending
+        w = OX.quantize(P_row[: I + 1])
+        J = np.arange(I + 1)
+        order = np.lexsort((-J, -w))
+        cs = np.cumsum(w[order])
+        k = int(np.argmax(cs * td >= tn * int(cs[-1])))
+        m = np.zeros(I + 1, dtype=bool)
+        m[order[: k + 1]] = True
+        m[0] = m[I] = True
+        return m
+    monkeypatch.setattr(OX, "select_row", desc_ties)
+    with pytest.raises(AssertionError):
+        TX.test_zero_query_selection_excludes_29_30()
+    monkeypatch.setattr(OX, "select_row", orig)
+
+
+def test_mutant_pooling_without_one_over_r(monkeypatch):
+    orig = OX.block_mass
+
+    def no_r(qh, kg, S, B, scale, *a, **kw):
+        return orig(qh, kg, S, B, scale, *a, **kw) * (B // S)   # planted: missing 1/r
+    monkeypatch.setattr(OX, "block_mass", no_r)
+    with pytest.raises(AssertionError):
+        TX.test_row_normalization()
+
+
+def test_mutant_ssa_pairs_sink_double_counted(monkeypatch):
+    def double(L, sink, window):
+        i = np.arange(L, dtype=np.int64)
+        lo = np.maximum(i - window + 1, 0)
+        return int((np.minimum(i + 1, sink) + (i - lo + 1)).sum())   # planted: overlap counted twice
+    monkeypatch.setattr(OR, "ssa_kept_pairs", double)
+    with pytest.raises(AssertionError):
+        TR.test_ssa_pairs_brute_and_closed_form(300, 7, 40)

@@ -1,0 +1,125 @@
+// Device-side utilities shared by the kernels of libea.so (gfx950, wave64).
+#pragma once
+
+#include "ea_internal.h"
+
+namespace ea {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// Inclusive prefix sum inside a wavefront (64 lanes).
+template <typename T>
+__device__ inline T wave_inclusive_sum(T v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ inline T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T>
+__device__ inline T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T u = __shfl_xor(v, o, 64);
+    v = u > v ? u : v;
+  }
+  return v;
+}
+
+// Block-wide exclusive prefix sum for blocks of NT threads (NT % 64 == 0).
+// `smem` needs NT / 64 + 1 elements.  Returns the exclusive prefix of the
+// calling thread; *total receives the block sum.  Contains barriers: every
+// thread of the block must call it.
+template <int NT, typename T>
+__device__ inline T block_exclusive_sum(T v, T* smem, T* total) {
+  constexpr int NW = NT / 64;
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  T inc = wave_inclusive_sum(v);
+  if (lane == 63) smem[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    T acc = 0;
+    for (int i = 0; i < NW; ++i) {
+      T t = smem[i];
+      smem[i] = acc;
+      acc += t;
+    }
+    smem[NW] = acc;
+  }
+  __syncthreads();
+  T res = smem[w] + inc - v;
+  *total = smem[NW];
+  __syncthreads();
+  return res;
+}
+
+// Block-wide exclusive prefix maximum (identity `lo`), same contract as above.
+template <int NT, typename T>
+__device__ inline T block_exclusive_max(T v, T lo, T* smem) {
+  constexpr int NW = NT / 64;
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  T inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T u = __shfl_up(inc, o, 64);
+    if (lane >= o) inc = u > inc ? u : inc;
+  }
+  T exc = __shfl_up(inc, 1, 64);
+  if (lane == 0) exc = lo;
+  if (lane == 63) smem[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    T acc = lo;
+    for (int i = 0; i < NW; ++i) {
+      T t = smem[i];
+      smem[i] = acc;
+      acc = t > acc ? t : acc;
+    }
+  }
+  __syncthreads();
+  T res = smem[w] > exc ? smem[w] : exc;
+  __syncthreads();
+  return res;
+}
+
+template <int NT, typename T>
+__device__ inline T block_sum(T v, T* smem) {
+  T tot;
+  block_exclusive_sum<NT, T>(v, smem, &tot);
+  return tot;
+}
+
+// Largest index p in [0, n) with a[p] <= x, for nondecreasing a with a[0] <= x.
+template <typename T>
+__device__ inline int upper_index(const T* a, int n, T x) {
+  int lo = 0, hi = n;  // a[lo] <= x, answer in [lo, hi)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace ea

@@ -1,0 +1,88 @@
+// Internal declarations shared by the translation units of libea.so.
+//
+// Host side: derived sizes (EaDims), the workspace layout, and the launchers
+// each .hip file exports.  Device side: small vector types and helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ea.h"
+
+namespace ea {
+
+// Sizes derived from a validated descriptor.  Every bound below depends on
+// the descriptor only, so the host can size buffers without reading device
+// data (cu_seqlens lives on the device).
+struct EaDims {
+  int32_t nseq, T, maxL, Hq, Hkv, G, D, B, S, r;  // r = B / S reduced rows per block
+  float scale;
+  int32_t sink, window, tau_num, tau_den;
+  int64_t nqb_max;  // bound on sum_b ceil(L_b / B):  T / B + nseq
+  int32_t maxqb;    // ceil(maxL / B): bound on q-blocks (and kv-blocks) per sequence
+  int32_t words;    // ceil(maxqb / 32): uint32 words per mask row
+  int64_t tpad;     // nqb_max * B: padded token count of the transposed V
+  int64_t tri_max;  // bound on sum_b nQB_b (nQB_b + 1) / 2
+};
+
+// Per-sequence metadata, built on the device from cu_seqlens (sanitised).
+struct SeqMeta {
+  int32_t* start;       // [nseq] first token
+  int32_t* len;         // [nseq] clamped length
+  int32_t* qb_prefix;   // [nseq+1] exclusive prefix of ceil(len / B)
+  int64_t* tri_prefix;  // [nseq+1] exclusive prefix of nQB (nQB + 1) / 2
+  int32_t* qb2seq;      // [nqb_max] global q-block -> sequence
+  int32_t* scal;        // [16] scalars, see SCAL_* below
+};
+
+enum {
+  SCAL_TOTAL_QB = 0,  // sum_b ceil(L_b / B)
+  SCAL_XA_PAIRS = 1,  // number of XA (sequence, q-head) pairs that score
+  SCAL_N_UNITS = 3,   // total_qb * Hkv
+  SCAL_CTR64 = 4,     // int64 work counter of the persistent scoring kernel (words 4..5)
+  SCAL_COUNT = 16
+};
+
+// Byte offsets of every workspace buffer (256-byte aligned).
+struct WsLayout {
+  size_t seq_start, seq_len, qb_prefix, tri_prefix, qb2seq, scal;
+  // XA select
+  size_t xa_pair_bh, xa_pair_items, xa_lse;
+  // prefill
+  size_t vt, unit_cost, row_cost, row_off, hist, cursor, sorted_units, tiles;
+  size_t total;
+};
+
+size_t ws_layout(const EaDims& d, int op, WsLayout* out);
+SeqMeta seq_meta_ptrs(const WsLayout& L, void* ws);
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----
+hipError_t launch_seq_meta(const EaDims& d, const int32_t* cu, const uint8_t* modes,
+                           const SeqMeta& m, void* ws, const WsLayout& L, bool for_select,
+                           int64_t* xa_pairs_out, hipStream_t st);
+hipError_t launch_xa_score(const EaDims& d, const uint16_t* q, const uint16_t* k,
+                           const SeqMeta& m, void* ws, const WsLayout& L, hipStream_t st);
+hipError_t launch_xa_select(const EaDims& d, const uint8_t* modes, const SeqMeta& m, void* ws,
+                            const WsLayout& L, uint32_t* mask, int32_t* row_count,
+                            int64_t* xa_pairs, float* block_mass, hipStream_t st);
+hipError_t launch_worklist(const EaDims& d, const uint16_t* v, const uint8_t* modes,
+                           const uint32_t* xa_mask, const SeqMeta& m, void* ws,
+                           const WsLayout& L, hipStream_t st);
+hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint16_t* k,
+                            const uint8_t* modes, const SeqMeta& m, void* ws,
+                            const WsLayout& L, uint16_t* o, float* lse, hipStream_t st);
+
+// ---- helpers usable on host and device ----
+__host__ __device__ inline int64_t tri64(int64_t n) { return n * (n + 1) / 2; }
+__host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+// Tile-list entry: kv-block index in the low 31 bits, bit 31 = needs a mask.
+constexpr uint32_t TILE_MASK_FLAG = 0x80000000u;
+
+// Sanitised mode byte: anything but SSA / XA runs as FA.
+__host__ __device__ inline int sane_mode(uint8_t m) {
+  return (m == EA_MODE_SSA || m == EA_MODE_XA) ? (int)m : (int)EA_MODE_FA;
+}
+
+}  // namespace ea

@@ -1,0 +1,268 @@
+// Work-list builder of the fused prefill: one flat list of kv tiles for
+// every (q-block, q-head) row of every mode, plus a longest-first schedule.
+//
+//   k_vt     V [T,Hkv,d] -> V^T [Hkv][d][padded tokens], keys permuted inside
+//            each 32-key group to match the MFMA operand order of the
+//            attention kernel, zero past the end of every sequence.
+//   k_cost   tiles per row (FA: I+1, SSA: sink + window blocks, XA: mask
+//            popcount); per unit (q-block, KV head) the max over its GQA
+//            siblings; histogram of unit costs.
+//   k_sched  one workgroup: counting sort of units by cost, descending, and
+//            the exclusive scan of row costs (row offsets into the list).
+//   k_fill   one wave per row writes its kv-block indices, each flagged when
+//            the tile needs a token-level mask (diagonal, window edge, sink
+//            edge, ragged sequence end).
+#include "ea_device.h"
+
+namespace ea {
+
+struct RowInfo {
+  int32_t b, I, len, mode;
+};
+
+__device__ inline RowInfo decode_qb(const EaDims& d, const SeqMeta& m, int32_t qbg, int g,
+                                    const uint8_t* modes, const uint32_t* xa_mask) {
+  RowInfo r;
+  r.b = m.qb2seq[qbg];
+  r.I = qbg - m.qb_prefix[r.b];
+  r.len = m.len[r.b];
+  r.mode = sane_mode(modes[(int64_t)r.b * d.Hkv + g]);
+  if (r.mode == EA_MODE_XA && xa_mask == nullptr) r.mode = EA_MODE_FA;
+  return r;
+}
+
+// First window block and number of sink-only blocks of an SSA row.
+__device__ inline void ssa_ranges(const EaDims& d, int32_t I, int32_t* jlo, int32_t* ns) {
+  const int64_t first = (int64_t)I * d.B - d.window + 1;  // window start of the first query
+  const int32_t lo = first <= 0 ? 0 : (int32_t)(first / d.B);
+  *jlo = lo;
+  *ns = min(cdiv(d.sink, d.B), lo);
+}
+
+// Does tile (I, J) of a row need a token-level mask?
+__device__ inline bool tile_needs_mask(const EaDims& d, int mode, int32_t I, int32_t J,
+                                       int32_t len) {
+  const int64_t i0 = (int64_t)I * d.B;
+  const int64_t ilast = min<int64_t>(i0 + d.B - 1, len - 1);
+  const int64_t j0 = (int64_t)J * d.B, j1 = j0 + d.B - 1;
+  if (J >= I) return true;               // diagonal (J > I never listed)
+  if (j1 >= len) return true;            // keys past the sequence end
+  if (mode == EA_MODE_SSA) {
+    const bool all_sink = j1 < d.sink;
+    const bool all_window = ilast - j0 < d.window;
+    return !(all_sink || all_window);
+  }
+  return false;
+}
+
+__device__ inline int swap_bits23(int p) {
+  return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+
+// ---------------------------------------------------------------- k_vt
+template <int D, int B>
+__global__ __launch_bounds__(256) void k_vt(EaDims d, const uint16_t* __restrict__ v, SeqMeta m,
+                                            uint16_t* __restrict__ vt) {
+  __shared__ uint16_t tile[B][D + 2];
+  const int32_t qbg = blockIdx.x;
+  if (qbg >= m.scal[SCAL_TOTAL_QB]) return;
+  const int g = blockIdx.y;
+  const int32_t b = m.qb2seq[qbg];
+  const int32_t J = qbg - m.qb_prefix[b];
+  const int32_t len = m.len[b];
+  const int64_t tok0 = (int64_t)m.start[b] + (int64_t)J * B;
+  const int32_t nvalid = min(B, len - J * B);
+  // Load rows (keys) as 16-byte chunks.
+  constexpr int CPR = D / 8;  // chunks per row
+  for (int c = threadIdx.x; c < B * CPR; c += 256) {
+    const int key = c / CPR, ch = c % CPR;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (key < nvalid)
+      val = *(const uint4*)(v + ((tok0 + key) * d.Hkv + g) * D + ch * 8);
+    const uint16_t* pv = (const uint16_t*)&val;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[key][ch * 8 + e] = pv[e];
+  }
+  __syncthreads();
+  // Write V^T rows: 8 consecutive (permuted) key positions per thread.
+  constexpr int CPD = B / 8;
+  for (int c = threadIdx.x; c < D * CPD; c += 256) {
+    const int dd = c / CPD, p0 = (c % CPD) * 8;
+    uint16_t outv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = p0 + e;
+      const int key = (p & ~31) | swap_bits23(p & 31);
+      outv[e] = tile[key][dd];
+    }
+    *(uint4*)(vt + ((int64_t)g * D + dd) * d.tpad + (int64_t)qbg * B + p0) = *(const uint4*)outv;
+  }
+}
+
+// ---------------------------------------------------------------- k_cost
+__global__ __launch_bounds__(256) void k_cost(EaDims d, const uint8_t* __restrict__ modes,
+                                              const uint32_t* __restrict__ xa_mask, SeqMeta m,
+                                              int32_t* __restrict__ unit_cost,
+                                              int32_t* __restrict__ row_cost,
+                                              int32_t* __restrict__ hist) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= m.scal[SCAL_N_UNITS]) return;
+  const int32_t qbg = (int32_t)(u / d.Hkv);
+  const int g = (int)(u % d.Hkv);
+  const RowInfo ri = decode_qb(d, m, qbg, g, modes, xa_mask);
+  int32_t uc = 0;
+  for (int k = 0; k < d.G; ++k) {
+    const int h = g * d.G + k;
+    int32_t c;
+    if (ri.mode == EA_MODE_SSA) {
+      int32_t jlo, ns;
+      ssa_ranges(d, ri.I, &jlo, &ns);
+      c = ns + ri.I - jlo + 1;
+    } else if (ri.mode == EA_MODE_XA) {
+      const uint32_t* row = xa_mask + ((int64_t)qbg * d.Hq + h) * d.words;
+      c = 0;
+      for (int w = 0; w * 32 <= ri.I; ++w) {
+        uint32_t bits = row[w];
+        const int hi = ri.I - w * 32;  // keep J <= I
+        if (hi < 31) bits &= (2u << hi) - 1u;
+        c += __popc(bits);
+      }
+    } else {
+      c = ri.I + 1;
+    }
+    row_cost[u * d.G + k] = c;
+    uc = max(uc, c);
+  }
+  unit_cost[u] = uc;
+  atomicAdd(&hist[uc], 1);
+}
+
+// ---------------------------------------------------------------- k_sched
+constexpr int SCHED_NT = 1024;
+
+__global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
+                                                    const int32_t* __restrict__ unit_cost,
+                                                    const int32_t* __restrict__ row_cost,
+                                                    const int32_t* __restrict__ hist,
+                                                    int32_t* __restrict__ cursor,
+                                                    int32_t* __restrict__ sorted_units,
+                                                    int64_t* __restrict__ row_off) {
+  __shared__ int64_t sm[SCHED_NT / 64 + 1];
+  const int tid = threadIdx.x;
+  const int32_t nb = d.maxqb + 1;  // costs 0..maxqb
+  // Bucket starts in descending cost order: cursor[c] = sum_{c' > c} hist[c'].
+  {
+    const int chunk = (nb + SCHED_NT - 1) / SCHED_NT;
+    const int i0 = min(nb, tid * chunk), i1 = min(nb, i0 + chunk);
+    int64_t s = 0;
+    for (int i = i0; i < i1; ++i) s += hist[d.maxqb - i];
+    int64_t tot;
+    int64_t e = block_exclusive_sum<SCHED_NT>(s, sm, &tot);
+    for (int i = i0; i < i1; ++i) {
+      cursor[d.maxqb - i] = (int32_t)e;
+      e += hist[d.maxqb - i];
+    }
+  }
+  __syncthreads();
+  const int32_t nu = m.scal[SCAL_N_UNITS];
+  for (int32_t u = tid; u < nu; u += SCHED_NT) {
+    const int32_t pos = atomicAdd(&cursor[unit_cost[u]], 1);
+    sorted_units[pos] = u;
+  }
+  // Row offsets into the flat tile list (natural row order).
+  const int64_t nr = (int64_t)nu * d.G;
+  const int64_t chunk = (nr + SCHED_NT - 1) / SCHED_NT;
+  const int64_t r0 = min(nr, tid * chunk), r1 = min(nr, r0 + chunk);
+  int64_t s = 0;
+  for (int64_t r = r0; r < r1; ++r) s += row_cost[r];
+  int64_t tot;
+  int64_t e = block_exclusive_sum<SCHED_NT>(s, sm, &tot);
+  for (int64_t r = r0; r < r1; ++r) {
+    row_off[r] = e;
+    e += row_cost[r];
+  }
+  if (tid == 0) row_off[nr] = tot;
+}
+
+// ---------------------------------------------------------------- k_fill
+__global__ __launch_bounds__(256) void k_fill(EaDims d, const uint8_t* __restrict__ modes,
+                                              const uint32_t* __restrict__ xa_mask, SeqMeta m,
+                                              const int32_t* __restrict__ row_cost,
+                                              const int64_t* __restrict__ row_off,
+                                              uint32_t* __restrict__ tiles) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= (int64_t)m.scal[SCAL_N_UNITS] * d.G) return;
+  const int64_t u = row / d.G;
+  const int k = (int)(row % d.G);
+  const int32_t qbg = (int32_t)(u / d.Hkv);
+  const int g = (int)(u % d.Hkv);
+  const int h = g * d.G + k;
+  const RowInfo ri = decode_qb(d, m, qbg, g, modes, xa_mask);
+  const int64_t off = row_off[row];
+  const int32_t cnt = row_cost[row];
+  uint32_t* out = tiles + off;
+  if (ri.mode == EA_MODE_XA) {
+    const uint32_t* mrow = xa_mask + ((int64_t)qbg * d.Hq + h) * d.words;
+    const int nw = ri.I / 32 + 1;
+    int32_t base = 0;
+    for (int w0 = 0; w0 < nw; w0 += 64) {
+      const int w = w0 + lane;
+      uint32_t bits = 0;
+      if (w < nw) {
+        bits = mrow[w];
+        const int hi = ri.I - w * 32;
+        if (hi < 31) bits &= (2u << hi) - 1u;
+      }
+      const int32_t pc = __popc(bits);
+      const int32_t inc = wave_inclusive_sum(pc);
+      int32_t pos = base + inc - pc;
+      while (bits) {
+        const int t = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const int32_t J = w * 32 + t;
+        out[pos++] = (uint32_t)J | (tile_needs_mask(d, ri.mode, ri.I, J, ri.len) ? TILE_MASK_FLAG : 0u);
+      }
+      base += __shfl(inc, 63, 64);
+    }
+    return;
+  }
+  int32_t jlo = 0, ns = 0;
+  if (ri.mode == EA_MODE_SSA) ssa_ranges(d, ri.I, &jlo, &ns);
+  for (int32_t t = lane; t < cnt; t += 64) {
+    int32_t J;
+    if (ri.mode == EA_MODE_SSA) J = t < ns ? t : jlo + (t - ns);
+    else J = t;
+    out[t] = (uint32_t)J | (tile_needs_mask(d, ri.mode, ri.I, J, ri.len) ? TILE_MASK_FLAG : 0u);
+  }
+}
+
+hipError_t launch_worklist(const EaDims& d, const uint16_t* v, const uint8_t* modes,
+                           const uint32_t* xa_mask, const SeqMeta& m, void* ws, const WsLayout& L,
+                           hipStream_t st) {
+  char* w = (char*)ws;
+  uint16_t* vt = (uint16_t*)(w + L.vt);
+  int32_t* unit_cost = (int32_t*)(w + L.unit_cost);
+  int32_t* row_cost = (int32_t*)(w + L.row_cost);
+  int64_t* row_off = (int64_t*)(w + L.row_off);
+  int32_t* hist = (int32_t*)(w + L.hist);
+  int32_t* cursor = (int32_t*)(w + L.cursor);
+  int32_t* sorted_units = (int32_t*)(w + L.sorted_units);
+  uint32_t* tiles = (uint32_t*)(w + L.tiles);
+  const dim3 gvt((unsigned)d.nqb_max, (unsigned)d.Hkv);
+  if (d.D == 128 && d.B == 128) hipLaunchKernelGGL((k_vt<128, 128>), gvt, dim3(256), 0, st, d, v, m, vt);
+  else if (d.D == 128 && d.B == 64) hipLaunchKernelGGL((k_vt<128, 64>), gvt, dim3(256), 0, st, d, v, m, vt);
+  else if (d.D == 64 && d.B == 128) hipLaunchKernelGGL((k_vt<64, 128>), gvt, dim3(256), 0, st, d, v, m, vt);
+  else hipLaunchKernelGGL((k_vt<64, 64>), gvt, dim3(256), 0, st, d, v, m, vt);
+  const int64_t units = d.nqb_max * d.Hkv;
+  hipLaunchKernelGGL(k_cost, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, d, modes,
+                     xa_mask, m, unit_cost, row_cost, hist);
+  hipLaunchKernelGGL(k_sched, dim3(1), dim3(SCHED_NT), 0, st, d, m, unit_cost, row_cost, hist,
+                     cursor, sorted_units, row_off);
+  const int64_t rows = d.nqb_max * d.Hq;
+  hipLaunchKernelGGL(k_fill, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, d, modes, xa_mask,
+                     m, row_cost, row_off, tiles);
+  return hipGetLastError();
+}
+
+}  // namespace ea

@@ -1,0 +1,164 @@
+"""ctypes binding of libea.so (include/ea.h), argument marshalling only.
+
+Each function here has the name of the C entry point it wraps and does
+nothing but convert arguments: torch tensors become raw pointers (data_ptr),
+the stream defaults to torch's current stream, and a status other than EA_OK
+raises EaError.  Every step of the computation runs in the HIP library.
+There is no fallback: if libea.so is missing, loading it raises.
+"""
+
+import ctypes
+import os
+
+EA_OK = 0
+EA_ERR_INVALID_ARG = 1
+EA_ERR_UNSUPPORTED = 2
+EA_ERR_WORKSPACE = 3
+EA_ERR_HIP = 4
+
+EA_MODE_FA = 0
+EA_MODE_SSA = 1
+EA_MODE_XA = 2
+
+EA_OP_XA_SELECT = 0
+EA_OP_PREFILL = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libea.so")
+
+# Every symbol include/ea.h declares.
+EXPORTS = (
+    "ea_workspace_bytes", "ea_mask_rows", "ea_mask_words", "ea_workspace_offset",
+    "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_sparsity_ratios", "ea_status_string",
+)
+
+
+class EaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("ssa_sink", ctypes.c_int32), ("ssa_window", ctypes.c_int32),
+        ("xa_stride", ctypes.c_int32), ("xa_tau_num", ctypes.c_int32),
+        ("xa_tau_den", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """Load libea.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m hybrid_sparse_full_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(AttnDesc)
+    L.ea_workspace_bytes.argtypes = [D, ctypes.c_int]
+    L.ea_workspace_bytes.restype = ctypes.c_size_t
+    L.ea_mask_rows.argtypes = [D]
+    L.ea_mask_rows.restype = ctypes.c_int64
+    L.ea_mask_words.argtypes = [D]
+    L.ea_mask_words.restype = ctypes.c_int32
+    L.ea_workspace_offset.argtypes = [D, ctypes.c_int, ctypes.c_char_p]
+    L.ea_workspace_offset.restype = ctypes.c_int64
+    L.ea_xa_block_select.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.ea_xa_block_select.restype = ctypes.c_int
+    L.ea_hybrid_attn_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.ea_hybrid_attn_prefill.restype = ctypes.c_int
+    L.ea_sparsity_ratios.argtypes = [D, P, P, ctypes.c_uint8, P, P, P, P, P]
+    L.ea_sparsity_ratios.restype = ctypes.c_int
+    L.ea_status_string.argtypes = [ctypes.c_int]
+    L.ea_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(x):
+    """Raw address of a tensor / numpy array / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def status_string(status):
+    return lib().ea_status_string(int(status)).decode()
+
+
+def ea_workspace_bytes(desc, op):
+    return int(lib().ea_workspace_bytes(ctypes.byref(desc), int(op)))
+
+
+def ea_mask_rows(desc):
+    return int(lib().ea_mask_rows(ctypes.byref(desc)))
+
+
+def ea_mask_words(desc):
+    return int(lib().ea_mask_words(ctypes.byref(desc)))
+
+
+def ea_workspace_offset(desc, op, name):
+    return int(lib().ea_workspace_offset(ctypes.byref(desc), int(op), name.encode()))
+
+
+def ea_xa_block_select(desc, q, k, cu_seqlens, modes, mask_out, row_count_out, xa_pairs_out,
+                       block_mass_out, workspace, stream=None):
+    st = lib().ea_xa_block_select(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(cu_seqlens), _ptr(modes), _ptr(mask_out),
+        _ptr(row_count_out), _ptr(xa_pairs_out), _ptr(block_mass_out), _ptr(workspace),
+        _nbytes(workspace) if workspace is not None else 0, _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_xa_block_select")
+
+
+def ea_hybrid_attn_prefill(desc, q, k, v, cu_seqlens, modes, xa_mask, o_out, lse_out, workspace,
+                           stream=None):
+    st = lib().ea_hybrid_attn_prefill(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(modes),
+        _ptr(xa_mask), _ptr(o_out), _ptr(lse_out), _ptr(workspace),
+        _nbytes(workspace) if workspace is not None else 0, _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_hybrid_attn_prefill")
+
+
+def ea_sparsity_ratios(desc, cu_seqlens_host, modes_host, sparse_mode, xa_pairs_host,
+                       msr_out, esr_out, rho_out, esr_pair_weighted_out=None):
+    """Host arrays (numpy, C-contiguous) in and out."""
+    st = lib().ea_sparsity_ratios(
+        ctypes.byref(desc), _ptr(cu_seqlens_host), _ptr(modes_host), int(sparse_mode),
+        _ptr(xa_pairs_host), _ptr(msr_out), _ptr(esr_out), _ptr(rho_out),
+        _ptr(esr_pair_weighted_out))
+    if st != EA_OK:
+        raise EaError(st, "ea_sparsity_ratios")

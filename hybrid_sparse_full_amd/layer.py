@@ -1,0 +1,104 @@
+"""Device-memory plumbing around the C ABI: one hybrid-head prefill layer.
+
+`HybridPrefill` owns the workspaces and output buffers (torch tensors, so
+torch's caching allocator provides device memory and streams) and calls the
+two device entry points in order: ea_xa_block_select when some head is XA,
+then ea_hybrid_attn_prefill.  All arithmetic happens inside libea.so.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from . import ea as E
+
+
+def make_desc(*, num_seqs, total_tokens, max_seqlen, num_q_heads, num_kv_heads, head_dim,
+              block, softmax_scale=None, ssa_sink=128, ssa_window=2048, xa_stride=8,
+              xa_tau=(9, 10)):
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    return E.AttnDesc(int(num_seqs), int(total_tokens), int(max_seqlen), int(num_q_heads),
+                      int(num_kv_heads), int(head_dim), int(block), float(softmax_scale),
+                      int(ssa_sink), int(ssa_window), int(xa_stride), int(xa_tau[0]),
+                      int(xa_tau[1]))
+
+
+class HybridPrefill:
+    """One layer's buffers for a fixed descriptor.
+
+    cu_seqlens and modes are given as host numpy arrays; they are copied to
+    the device once here (the C ABI reads them on the device).
+    """
+
+    def __init__(self, desc, cu_seqlens, modes, device="cuda", block_mass=False):
+        self.desc = desc
+        self.device = torch.device(device)
+        self.cu_host = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        self.modes_host = np.ascontiguousarray(modes, dtype=np.uint8)
+        self.cu = torch.from_numpy(self.cu_host).to(self.device)
+        self.modes = torch.from_numpy(self.modes_host.reshape(-1)).to(self.device)
+        self.has_xa = bool((self.modes_host == E.EA_MODE_XA).any())
+        T, Hq, D = desc.total_tokens, desc.num_q_heads, desc.head_dim
+        self.o = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=self.device)
+        self.lse = torch.empty((Hq, T), dtype=torch.float32, device=self.device)
+        self.ws_prefill = torch.empty(E.ea_workspace_bytes(desc, E.EA_OP_PREFILL),
+                                      dtype=torch.uint8, device=self.device)
+        self.rows = E.ea_mask_rows(desc)
+        self.words = E.ea_mask_words(desc)
+        self.maxqb = -(-desc.max_seqlen // desc.block)
+        self.mask = self.row_count = self.xa_pairs = self.block_mass = self.ws_select = None
+        if self.has_xa:
+            self.ws_select = torch.empty(E.ea_workspace_bytes(desc, E.EA_OP_XA_SELECT),
+                                         dtype=torch.uint8, device=self.device)
+            self.mask = torch.empty((self.rows, self.words), dtype=torch.int32, device=self.device)
+            self.row_count = torch.empty(self.rows, dtype=torch.int32, device=self.device)
+            self.xa_pairs = torch.empty(desc.num_seqs * Hq, dtype=torch.int64, device=self.device)
+            if block_mass:
+                self.block_mass = torch.zeros((self.rows, self.maxqb), dtype=torch.float32,
+                                              device=self.device)
+
+    def select(self, q, k, stream=None):
+        E.ea_xa_block_select(self.desc, q, k, self.cu, self.modes, self.mask, self.row_count,
+                             self.xa_pairs, self.block_mass, self.ws_select, stream)
+
+    def prefill(self, q, k, v, stream=None):
+        E.ea_hybrid_attn_prefill(self.desc, q, k, v, self.cu, self.modes,
+                                 self.mask if self.has_xa else None, self.o, self.lse,
+                                 self.ws_prefill, stream)
+
+    def __call__(self, q, k, v, stream=None):
+        if self.has_xa:
+            self.select(q, k, stream)
+        self.prefill(q, k, v, stream)
+        return self.o, self.lse
+
+    def ratios(self, sparse_mode):
+        """Omega_MSR / Omega_ESR / rho on the host (needs the XA pair counts)."""
+        nseq, hkv = self.modes_host.shape
+        msr = np.zeros(nseq + 1)
+        esr = np.zeros(nseq + 1)
+        rho = np.zeros(nseq * hkv)
+        pw = np.zeros(1)
+        pairs = None
+        if self.has_xa:
+            pairs = np.ascontiguousarray(self.xa_pairs.cpu().numpy())
+        E.ea_sparsity_ratios(self.desc, self.cu_host, self.modes_host, sparse_mode, pairs,
+                             msr, esr, rho, pw)
+        return dict(msr=msr, esr=esr, rho=rho.reshape(nseq, hkv), esr_pairs=float(pw[0]))
+
+
+def bf16_tensor(bits, device):
+    """uint16 bf16 bit patterns (numpy) -> torch bfloat16 on `device`."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def desc_for(cfg, seqlens):
+    return make_desc(num_seqs=len(seqlens), total_tokens=int(np.sum(seqlens)),
+                     max_seqlen=int(np.max(seqlens)) if len(seqlens) else 0,
+                     num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
+                     head_dim=cfg.head_dim, block=cfg.block, softmax_scale=cfg.softmax_scale,
+                     ssa_sink=cfg.ssa_sink, ssa_window=cfg.ssa_window, xa_stride=cfg.xa_stride,
+                     xa_tau=(cfg.tau_num, cfg.tau_den))

@@ -1,0 +1,197 @@
+/*
+ * ea.h -- C ABI of libea.so: hybrid-head prefill attention (Elastic Attention)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One layer of causal prefill attention in which every KV head of every
+ * sequence runs in the mode an external router assigned to it:
+ *   FA  = full causal softmax attention (Eq. 1 of the Elastic Attention
+ *         paper-reading notes, "02 . Background"),
+ *   SSA = streaming sparse attention: attention sink plus sliding window
+ *         (glossary of the notes; Table 8 gives sink/local 128/2048),
+ *   XA  = block-sparse attention over blocks chosen by antidiagonal scoring
+ *         and a cumulative-mass threshold (glossary; Table 8 threshold 0.9).
+ * The layer output is the head-wise concatenation of the per-head outputs
+ * (Eq. 3).  The mode array plays the role of the routing metadata that the
+ * notes' deployment section passes to a single fused kernel launch.
+ *
+ * Conventions for every entry point
+ *   - Tensors are packed variable-length batches: q, o [T, Hq, d];
+ *     k, v [T, Hkv, d]; d contiguous, bfloat16.  lse [Hq, T] float32.
+ *     Sequence b owns tokens [cu_seqlens[b], cu_seqlens[b+1]).
+ *     GQA: query head h reads KV head h / (Hq / Hkv).
+ *   - q, k, v and o must be 16-byte aligned (EA_ERR_INVALID_ARG otherwise).
+ *   - Every pointer is owned by the caller.  "_dev" pointers are device
+ *     memory on the current HIP device; "_host" pointers are host memory.
+ *     The library allocates nothing, keeps no global state and is reentrant
+ *     as long as concurrent calls use different workspaces.
+ *   - All arguments that the host can see are checked before any launch;
+ *     on failure an ea_status other than EA_OK is returned and nothing is
+ *     written.  Device-side data (cu_seqlens, modes) cannot be checked
+ *     without a host synchronisation, so the kernels sanitise it instead:
+ *     lengths are clamped to [0, max_seqlen] and to the token range, mode
+ *     bytes other than 0/1/2 run as FA.  No input can make a kernel access
+ *     memory outside the documented buffers.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) without any host synchronisation.  A launch failure returns
+ *     EA_ERR_HIP.
+ */
+#ifndef EA_H
+#define EA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EA_OK = 0,
+  EA_ERR_INVALID_ARG = 1, /* null pointer, bad size or parameter */
+  EA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block, stride */
+  EA_ERR_WORKSPACE = 3,   /* workspace pointer null or too small */
+  EA_ERR_HIP = 4          /* a HIP launch failed */
+} ea_status;
+
+typedef enum { EA_MODE_FA = 0, EA_MODE_SSA = 1, EA_MODE_XA = 2 } ea_mode;
+
+typedef struct {
+  int32_t num_seqs;      /* >= 0 */
+  int32_t total_tokens;  /* T = cu_seqlens[num_seqs], >= 0 */
+  int32_t max_seqlen;    /* upper bound of every sequence length */
+  int32_t num_q_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t block;         /* B: 64 or 128; kernel tile and XA block size */
+  float softmax_scale;   /* c > 0, usually 1/sqrt(d) */
+  int32_t ssa_sink;      /* s >= 0: keys j < s are always kept by SSA */
+  int32_t ssa_window;    /* W >= 1: SSA keeps keys with i - j < W */
+  int32_t xa_stride;     /* S: divides B with B/S in {8, 16, 32} */
+  int32_t xa_tau_num;    /* tau = num/den, 0 < tau <= 1, den <= 2^20 */
+  int32_t xa_tau_den;
+} ea_attn_desc;
+
+/* Operation codes for ea_workspace_bytes. */
+#define EA_OP_XA_SELECT 0
+#define EA_OP_PREFILL 1
+
+/*
+ * Workspace bytes that `op` needs for `desc`: an upper bound computed from
+ * the descriptor alone (total_tokens, num_seqs, max_seqlen, heads, block).
+ * Returns 0 if the descriptor is invalid or unsupported.
+ */
+size_t ea_workspace_bytes(const ea_attn_desc* desc, int op);
+
+/*
+ * Mask geometry shared by ea_xa_block_select and ea_hybrid_attn_prefill.
+ * Mask rows are indexed by (global q-block, q-head): row = (P_b + I) * Hq + h,
+ * where P_b = sum_{b' < b} ceil(L_b' / B) and I is the q-block within
+ * sequence b.  Each row holds ea_mask_words(desc) uint32 words; bit J of the
+ * row (word J / 32, bit J % 32) set means KV block J is attended.
+ * ea_mask_rows(desc) = (T / B + num_seqs) * Hq is the row count the caller
+ * allocates (an upper bound of the rows that exist).  Both return 0 for an
+ * invalid descriptor.
+ */
+int64_t ea_mask_rows(const ea_attn_desc* desc);
+int32_t ea_mask_words(const ea_attn_desc* desc);
+
+/*
+ * XA block selection (scoring + selector) for every XA (sequence, q-head).
+ *
+ * Defines XA's "which blocks" step (glossary of the Elastic Attention notes:
+ * antidiagonal scoring; Table 8: block / stride / threshold):
+ *   score   s^[a, b'] = c * sum_{t<S} <q_{aS+t}, k_{b'S+S-1-t}>  for b' <= a
+ *           (a, b' index groups of S tokens inside the sequence),
+ *   p[a, .] = softmax over b' <= a of s^[a, .],
+ *   P[I, J] = (1 / (B/S)) * sum of p over the (a, b') pairs of block (I, J),
+ *   w_J     = max(1, floor(P[I, J] * 2^24 + 1/2)),
+ *   select  the shortest prefix of J sorted by (w desc, J asc) whose integer
+ *           mass reaches tau * sum_J w_J, then add J = 0 and J = I.
+ * Each q-head scores and selects its own mask; XA runs on sequences whose
+ * length is a multiple of B.  On an XA head of a sequence with L % B != 0,
+ * every causal block is selected (XA with tau = 1, which is FA).
+ *
+ * Inputs  q [T,Hq,d] bf16, k [T,Hkv,d] bf16, cu_seqlens_dev int32[num_seqs+1],
+ *         modes_dev uint8[num_seqs * Hkv] (row-major [seq][kv head]).
+ * Outputs (device; every row of every q-head is written)
+ *   mask_out_dev       uint32[ea_mask_rows][ea_mask_words]; rows of non-XA
+ *                      heads are written as all-zero.
+ *   row_count_out_dev  int32[ea_mask_rows]: selected blocks per row (0 for
+ *                      non-XA heads).
+ *   xa_pairs_out_dev   int64[num_seqs * Hq]: attended (i, j) pairs per
+ *                      (sequence, q-head); 0 for non-XA heads.
+ *   block_mass_out_dev float32[ea_mask_rows][ceil(max_seqlen / B)] or NULL:
+ *                      P[I, J] of XA rows for J <= I, zero for J > I; rows
+ *                      of other heads are not touched.
+ * Workspace: ea_workspace_bytes(desc, EA_OP_XA_SELECT) bytes, device memory.
+ */
+ea_status ea_xa_block_select(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
+                             const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                             uint32_t* mask_out_dev, int32_t* row_count_out_dev,
+                             int64_t* xa_pairs_out_dev, float* block_mass_out_dev,
+                             void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused hybrid-head prefill attention (Eqs. 1-3 of the notes; one launch of
+ * the attention kernel serves FA, SSA and XA heads together).
+ *
+ * For query i of sequence b (local index) and q-head h with KV head g:
+ *   A(i) = { j <= i }                                   if mode FA
+ *        = { j <= i : j < ssa_sink or i - j < ssa_window }   if mode SSA
+ *        = { j <= i : mask bit (I = i / B, J = j / B) set }  if mode XA
+ *   o_i  = sum_{j in A(i)} softmax_j(c <q_i, k_j>) v_j,
+ *   lse_i = ln sum_{j in A(i)} exp(c <q_i, k_j>).
+ * Outputs  o_out_dev [T,Hq,d] bf16 (round to nearest even from fp32) and
+ *          lse_out_dev [Hq,T] float32.  Every token of every head is written.
+ *          A query whose key set is empty (possible only with a caller-made
+ *          XA mask that lacks its diagonal block) gets o = 0, lse = -inf.
+ * xa_mask_dev: the mask written by ea_xa_block_select for the same inputs.
+ *          If NULL, XA heads attend every causal block.
+ * Workspace: ea_workspace_bytes(desc, EA_OP_PREFILL) bytes, device memory.
+ */
+ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
+                                 const void* v_dev, const int32_t* cu_seqlens_dev,
+                                 const uint8_t* modes_dev, const uint32_t* xa_mask_dev,
+                                 void* o_out_dev, float* lse_out_dev, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Model and effective sparsity ratios (Eq. 4 and Eq. 5 of the Chinese
+ * paper-reading notes, section on the two sparsity ratios), computed on the
+ * host, synchronously.  One layer; the average runs over the KV heads of a
+ * sequence, and the batch value is the mean over sequences.
+ *   Omega_MSR(b) = mean_g [modes[b,g] == sparse_mode]
+ *   rho(b,g)     = 1 - kept pairs of the G q-heads of g / (G * L_b (L_b+1) / 2)
+ *                  (0 for FA; SSA counted from its key set; XA from xa_pairs)
+ *   Omega_ESR(b) = mean_g rho(b, g)
+ * Inputs (host): cu_seqlens_host int32[num_seqs+1] (nondecreasing, from 0),
+ *   modes_host uint8[num_seqs*Hkv] (values 0..2), sparse_mode 0..2 names the
+ *   "sparse" slot of the {retrieval}-{sparse} mode set, xa_pairs_host
+ *   int64[num_seqs*Hq] as written by ea_xa_block_select (may be NULL only if
+ *   no head is XA).
+ * Outputs (host): msr_out and esr_out double[num_seqs+1] (per sequence, then
+ *   the batch mean), rho_out double[num_seqs*Hkv], esr_pair_weighted_out
+ *   double[1] or NULL (1 - total kept / total causal pairs).
+ */
+ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu_seqlens_host,
+                             const uint8_t* modes_host, uint8_t sparse_mode,
+                             const int64_t* xa_pairs_host, double* msr_out, double* esr_out,
+                             double* rho_out, double* esr_pair_weighted_out);
+
+/*
+ * Diagnostics: byte offset of a named internal buffer inside the workspace of
+ * `op` (for example "tiles", "row_off", "row_cost", "sorted_units" of the
+ * prefill work list, "xa_lse" of the selector), or -1 if the name is unknown
+ * for that operation or the descriptor is invalid.  The layout is an
+ * implementation detail; this exists so that tests can check the work list.
+ */
+int64_t ea_workspace_offset(const ea_attn_desc* desc, int op, const char* name);
+
+/* Static string naming a status code. */
+const char* ea_status_string(ea_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EA_H */

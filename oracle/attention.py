@@ -123,6 +123,18 @@ def prefill(q, k, v, cu_seqlens, modes, *, scale, block, sink, window,
     return O, LSE
 
 
+def row_attention(q_i, k_seq, v_seq, i, mode, scale, *, sink=0, window=1, block=None,
+                  xa_mask=None):
+    """One query row: q_i [d], k_seq / v_seq [L, d] of the row's sequence and
+    KV head (float64), i the local query index.  Returns (o_i [d], lse_i)."""
+    L = k_seq.shape[0]
+    jj = _candidate_keys(mode, i, i + 1, sink, window)
+    allowed = allowed_matrix(mode, np.array([i]), jj, L, sink, window, block, xa_mask)
+    s = scale * (k_seq[jj] @ q_i)[None, :]
+    o, lse = _softmax_rows(s, allowed, v_seq[jj])
+    return o[0], lse[0]
+
+
 def prefill_rows(q, k, v, cu_seqlens, modes, rows, *, scale, block, sink, window,
                  xa_masks=None):
     """Selected query rows only: rows is a list of (b, h, i) with i local.
@@ -136,14 +148,9 @@ def prefill_rows(q, k, v, cu_seqlens, modes, rows, *, scale, block, sink, window
     out_l = np.empty(len(rows))
     for n, (b, h, i) in enumerate(rows):
         t0, t1 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
-        L = t1 - t0
         g = h // G
         mode = int(modes[b, g])
         xm = xa_masks[(b, h)] if mode == MODE_XA else None
-        jj = _candidate_keys(mode, i, i + 1, sink, window)
-        allowed = allowed_matrix(mode, np.array([i]), jj, L, sink, window, block, xm)
-        s = scale * (q[t0 + i, h][None, :] @ k[t0 + jj, g].T)
-        o, lse = _softmax_rows(s, allowed, v[t0 + jj, g])
-        out_o[n] = o[0]
-        out_l[n] = lse[0]
+        out_o[n], out_l[n] = row_attention(q[t0 + i, h], k[t0:t1, g], v[t0:t1, g], i, mode, scale,
+                                           sink=sink, window=window, block=block, xa_mask=xm)
     return out_o, out_l

@@ -160,3 +160,18 @@ def kept_pairs(mask, L, B):
             else:
                 total += B * (B + 1) // 2
     return total
+
+
+def head_mask(qh, kg, S, B, scale, tau_num, tau_den, rows=None):
+    """XA block mask of one (sequence, q-head) and its block masses.
+
+    A sequence whose length is not a whole number of blocks gets every causal
+    block (the kernel library's stated rule; XA with tau = 1, i.e. FA), and
+    P is None.  `rows` restricts scoring and selection to those block rows.
+    """
+    L = qh.shape[0]
+    nb = -(-L // B)
+    if L % B:
+        return np.tril(np.ones((nb, nb), dtype=bool)), None
+    P = block_mass(qh, kg, S, B, scale, rows=rows)
+    return select(P, tau_num, tau_den, rows=rows), P

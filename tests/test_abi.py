@@ -1,0 +1,194 @@
+"""CPU tests of the C ABI: exported symbols, workspace sizing, argument
+validation (every case fails before any device work), and the host-side
+sparsity ratios against the oracle."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from hybrid_sparse_full_amd import ea as E
+from oracle import ratios as OR
+from synth import MODE_FA, MODE_SSA, MODE_XA
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced here
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ea.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ea_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_header_symbol():
+    names = header_functions()
+    assert "ea_hybrid_attn_prefill" in names and "ea_sparsity_ratios" in names
+    lib = E.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(E.EXPORTS)
+
+
+def desc(**kw):
+    base = dict(num_seqs=1, total_tokens=4096, max_seqlen=4096, num_q_heads=32, num_kv_heads=8,
+                head_dim=128, block=128, softmax_scale=128 ** -0.5, ssa_sink=128, ssa_window=2048,
+                xa_stride=8, xa_tau_num=9, xa_tau_den=10)
+    base.update(kw)
+    return E.AttnDesc(**base)
+
+
+def test_workspace_sizes():
+    d = desc()
+    for op in (E.EA_OP_PREFILL, E.EA_OP_XA_SELECT):
+        assert E.ea_workspace_bytes(d, op) > 0
+    assert E.ea_workspace_bytes(d, 7) == 0
+    assert E.ea_mask_words(d) == 1 and E.ea_mask_rows(d) == (4096 // 128 + 1) * 32
+    big = desc(total_tokens=262144, max_seqlen=262144)
+    assert E.ea_mask_words(big) == 64
+    assert E.ea_workspace_bytes(big, E.EA_OP_PREFILL) > E.ea_workspace_bytes(d, E.EA_OP_PREFILL)
+    assert E.ea_workspace_offset(d, E.EA_OP_PREFILL, "tiles") > 0
+    assert E.ea_workspace_offset(d, E.EA_OP_PREFILL, "xa_lse") == -1
+    assert E.ea_workspace_offset(d, E.EA_OP_XA_SELECT, "xa_lse") > 0
+
+
+BAD = [
+    (dict(num_q_heads=30), E.EA_ERR_INVALID_ARG),           # Hq % Hkv
+    (dict(num_kv_heads=0), E.EA_ERR_INVALID_ARG),
+    (dict(head_dim=96), E.EA_ERR_UNSUPPORTED),
+    (dict(block=32), E.EA_ERR_UNSUPPORTED),
+    (dict(ssa_window=0), E.EA_ERR_INVALID_ARG),
+    (dict(ssa_sink=-1), E.EA_ERR_INVALID_ARG),
+    (dict(xa_tau_num=11), E.EA_ERR_INVALID_ARG),            # tau > 1
+    (dict(xa_tau_num=0), E.EA_ERR_INVALID_ARG),             # tau = 0
+    (dict(xa_stride=3), E.EA_ERR_INVALID_ARG),              # stride does not divide block
+    (dict(xa_stride=64), E.EA_ERR_UNSUPPORTED),             # B/S = 2
+    (dict(softmax_scale=0.0), E.EA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), E.EA_ERR_INVALID_ARG),
+    (dict(max_seqlen=5000), E.EA_ERR_INVALID_ARG),          # longer than the batch
+    (dict(num_seqs=2, max_seqlen=1000), E.EA_ERR_INVALID_ARG),  # 2 * 1000 < 4096
+    (dict(num_seqs=0), E.EA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_prefill_rejects_bad_descriptor(kw, code):
+    lib = E.lib()
+    d = desc(**kw)
+    st = lib.ea_hybrid_attn_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                    FAKE, FAKE, 1 << 40, None)
+    assert st == code
+    st = lib.ea_xa_block_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                FAKE, 1 << 40, None)
+    assert st == code
+    assert E.ea_workspace_bytes(d, E.EA_OP_PREFILL) == 0
+
+
+def test_prefill_rejects_null_and_misaligned_and_small_workspace():
+    lib = E.lib()
+    d = desc()
+    need = E.ea_workspace_bytes(d, E.EA_OP_PREFILL)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None]
+    assert lib.ea_hybrid_attn_prefill(None, *args) == E.EA_ERR_INVALID_ARG
+    for i in (0, 1, 2, 3, 4, 6, 7):          # q k v cu modes o lse
+        a = list(args)
+        a[i] = None
+        assert lib.ea_hybrid_attn_prefill(ctypes.byref(d), *a) == E.EA_ERR_INVALID_ARG, i
+    for i in (0, 1, 2, 6):                   # q k v o need 16-byte alignment
+        a = list(args)
+        a[i] = FAKE + 2
+        assert lib.ea_hybrid_attn_prefill(ctypes.byref(d), *a) == E.EA_ERR_INVALID_ARG, i
+    a = list(args)
+    a[9] = need - 1
+    assert lib.ea_hybrid_attn_prefill(ctypes.byref(d), *a) == E.EA_ERR_WORKSPACE
+    a = list(args)
+    a[8] = None
+    assert lib.ea_hybrid_attn_prefill(ctypes.byref(d), *a) == E.EA_ERR_WORKSPACE
+    # Nothing to do: returns before any launch.
+    d0 = desc(total_tokens=0, max_seqlen=0)
+    need0 = E.ea_workspace_bytes(d0, E.EA_OP_PREFILL)
+    assert lib.ea_hybrid_attn_prefill(ctypes.byref(d0), None, None, None, FAKE, FAKE, None, None,
+                                      None, FAKE, need0, None) == E.EA_OK
+
+
+def test_select_rejects_small_workspace_and_nulls():
+    lib = E.lib()
+    d = desc()
+    need = E.ea_workspace_bytes(d, E.EA_OP_XA_SELECT)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, None]
+    for i in (0, 1, 2, 3, 4, 5, 6):          # q k cu modes mask count pairs
+        a = list(args)
+        a[i] = None
+        assert lib.ea_xa_block_select(ctypes.byref(d), *a) == E.EA_ERR_INVALID_ARG, i
+    a = list(args)
+    a[9] = need - 256
+    assert lib.ea_xa_block_select(ctypes.byref(d), *a) == E.EA_ERR_WORKSPACE
+
+
+def _ratios_c(d, cu, modes, sparse_mode, pairs):
+    nseq, hkv = modes.shape
+    msr, esr, rho, pw = np.zeros(nseq + 1), np.zeros(nseq + 1), np.zeros(nseq * hkv), np.zeros(1)
+    E.ea_sparsity_ratios(d, np.ascontiguousarray(cu, np.int32), np.ascontiguousarray(modes, np.uint8),
+                         sparse_mode, None if pairs is None else np.ascontiguousarray(pairs, np.int64),
+                         msr, esr, rho, pw)
+    return msr, esr, rho.reshape(nseq, hkv), pw[0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sparsity_ratios_match_oracle(seed):
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.integers(1, 6))
+    hkv, G = 4, int(rng.choice([1, 2, 4]))
+    seqlens = rng.integers(0, 3000, size=nseq)
+    modes = rng.integers(0, 3, size=(nseq, hkv)).astype(np.uint8)
+    sink, window = int(rng.integers(0, 300)), int(rng.integers(1, 2000))
+    pairs = np.zeros((nseq, hkv * G), dtype=np.int64)
+    for b in range(nseq):
+        causal = int(seqlens[b]) * (int(seqlens[b]) + 1) // 2
+        pairs[b] = rng.integers(0, causal + 1, size=hkv * G)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    d = desc(num_seqs=nseq, total_tokens=int(cu[-1]), max_seqlen=max(1, int(seqlens.max())),
+             num_q_heads=hkv * G, num_kv_heads=hkv, ssa_sink=sink, ssa_window=window)
+    sm = int(rng.integers(0, 3))
+    msr, esr, rho, pw = _ratios_c(d, cu, modes, sm, pairs)
+    ref = OR.sparsity_ratios(seqlens, modes, hkv * G, sink=sink, window=window, sparse_mode=sm,
+                             xa_pairs=pairs)
+    np.testing.assert_allclose(msr, ref["msr"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(esr, ref["esr"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(rho, ref["rho"], rtol=0, atol=1e-13)
+    assert abs(pw - ref["esr_pairs"]) < 1e-13
+
+
+def test_sparsity_ratios_rejects_bad_host_data():
+    d = desc(num_seqs=2, total_tokens=300, max_seqlen=200)
+    modes = np.array([[0, 1, 1, 1, 1, 1, 1, 1], [0, 1, 1, 1, 1, 1, 1, 1]], np.uint8)
+    ok_cu = np.array([0, 100, 300], np.int32)
+    _ratios_c(d, ok_cu, modes, MODE_SSA, None)
+    for cu in ([1, 100, 300], [0, 100, 299], [0, 250, 300], [0, 150, 100]):
+        with pytest.raises(E.EaError):
+            _ratios_c(d, np.array(cu, np.int32), modes, MODE_SSA, None)
+    bad = modes.copy()
+    bad[0, 0] = 3
+    with pytest.raises(E.EaError):
+        _ratios_c(d, ok_cu, bad, MODE_SSA, None)
+    xa = modes.copy()
+    xa[1, 2] = MODE_XA
+    with pytest.raises(E.EaError):                  # XA head but no pair counts
+        _ratios_c(d, ok_cu, xa, MODE_SSA, None)
+    pairs = np.zeros((2, 32), np.int64)
+    pairs[1, 8] = 10 ** 9                           # more pairs than causal
+    with pytest.raises(E.EaError):
+        _ratios_c(d, ok_cu, xa, MODE_SSA, pairs)
+
+
+def test_page_fact_ratios_through_c_abi():
+    # 10 % of the causal pairs kept -> rho = 0.9 (Eq. 5 worked example).
+    L = 1000
+    d = desc(num_seqs=1, total_tokens=L, max_seqlen=L, num_q_heads=2, num_kv_heads=2)
+    causal = L * (L + 1) // 2
+    pairs = np.array([[causal // 10, 0]], np.int64)
+    msr, esr, rho, pw = _ratios_c(d, np.array([0, L]), np.array([[MODE_XA, MODE_FA]], np.uint8),
+                                  MODE_XA, pairs)
+    assert abs(rho[0, 0] - 0.9) < 1e-12 and rho[0, 1] == 0 and msr[0] == 0.5

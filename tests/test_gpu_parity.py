@@ -67,14 +67,20 @@ def test_xa_masks_many_rows():
             assert gout["xa_pairs"][b, h] == OX.kept_pairs(M, L, cfg.block)
 
 
+def _all_fa(inp):
+    inp1 = dict(inp)
+    inp1["modes"] = np.zeros_like(inp["modes"])
+    return PU.run_gpu(inp1)
+
+
 def test_ssa_window_ge_len_is_bitwise_fa():
+    # SSA with window >= L keeps every causal key: the same heads of an all-FA
+    # run must be bit-identical.
     cfg = _small(seqlens=(700, 256), modes=((MODE_SSA, MODE_FA),), ssa_window=10 ** 6)
     inp = make_inputs(cfg)
     g = PU.run_gpu(inp)
-    G = cfg.gqa
-    for h in range(G):
-        assert np.array_equal(g["o"][:, h], g["o"][:, G + h])
-        assert np.array_equal(g["lse"][h], g["lse"][G + h])
+    f = _all_fa(inp)
+    assert np.array_equal(g["o"], f["o"]) and np.array_equal(g["lse"], f["lse"])
 
 
 def test_tau_one_is_bitwise_fa():
@@ -83,8 +89,8 @@ def test_tau_one_is_bitwise_fa():
     g = PU.run_gpu(inp)
     G = cfg.gqa
     assert g["row_count"].reshape(-1, cfg.num_q_heads)[:8, :G].sum() == 8 * 9 // 2 * G
-    for h in range(G):
-        assert np.array_equal(g["o"][:, h], g["o"][:, G + h])
+    f = _all_fa(inp)
+    assert np.array_equal(g["o"], f["o"]) and np.array_equal(g["lse"], f["lse"])
 
 
 def test_eq3_concatenation_bitwise():
@@ -112,7 +118,10 @@ def test_deterministic():
     a = PU.run_gpu(inp)
     b = PU.run_gpu(inp)
     assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
-    assert np.array_equal(a["mask"], b["mask"]) and np.array_equal(a["xa_pairs"], b["xa_pairs"])
+    # Mask rows past the last existing q-block are not part of the output.
+    nrows = int(PU.qb_prefix(inp["seqlens"], cfg.block)[-1]) * cfg.num_q_heads
+    assert np.array_equal(a["mask"][:nrows], b["mask"][:nrows])
+    assert np.array_equal(a["xa_pairs"], b["xa_pairs"])
 
 
 def _sampled_check(name, n_rows, seed, xa_rows_per_head=6):

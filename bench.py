@@ -64,20 +64,14 @@ def attended_pairs(inp, gpu_xa_pairs=None):
     return total
 
 
-def workspace_tiles(layer):
-    """Computed tiles of the last prefill, read from the work list it built."""
+def workspace_counts(layer):
+    """(tile-list entries, computed (tile, q-head) pairs) of the last prefill,
+    read from the counters its work-list build wrote into the workspace."""
     import torch
     from hybrid_sparse_full_amd import ea as E
-    d = layer.desc
-    off = E.ea_workspace_offset(d, E.EA_OP_PREFILL, "row_off")
-    nrows = (E.ea_mask_rows(d))  # upper bound; the exact count is in scal
-    scal_off = E.ea_workspace_offset(d, E.EA_OP_PREFILL, "scal")
-    scal = layer.ws_prefill[scal_off:scal_off + 64].view(torch.int32).cpu().numpy()
-    n_units = int(scal[3])
-    nr = n_units * (d.num_q_heads // d.num_kv_heads)
-    assert nr <= nrows
-    ro = layer.ws_prefill[off:off + 8 * (nr + 1)].view(torch.int64).cpu().numpy()
-    return int(ro[nr])
+    off = E.ea_workspace_offset(layer.desc, E.EA_OP_PREFILL, "scal")
+    scal = layer.ws_prefill[off:off + 64].view(torch.int64).cpu().numpy()
+    return int(scal[4]), int(scal[3])
 
 
 def time_steps(fn, steps, warmup):
@@ -128,7 +122,6 @@ def cpu_baseline(inp, seconds):
         if mode == 2:
             continue
         if (b, g) not in cache:
-            cache.clear()
             cache[(b, g)] = (bf16_bits_to_f64(inp["k"][cu[b]:cu[b + 1], g]),
                              bf16_bits_to_f64(inp["v"][cu[b]:cu[b + 1], g]))
         kg, vg = cache[(b, g)]
@@ -177,11 +170,11 @@ def main():
     if layer.has_xa:
         layer.select(q, k)
     _, attn_ms, _ = time_steps(lambda: layer.prefill(q, k, v), a.steps, 1)
-    tiles = workspace_tiles(layer)
+    tiles, head_tiles = workspace_counts(layer)
     xa_pairs = layer.xa_pairs.cpu().numpy().reshape(len(inp["seqlens"]), -1) if layer.has_xa else None
     pairs = attended_pairs(inp, xa_pairs)
     D, B = cfg.head_dim, cfg.block
-    tile_flops = 4.0 * B * B * D * tiles
+    tile_flops = 4.0 * B * B * D * head_tiles
     pair_flops = 4.0 * D * pairs
     T = int(inp["cu_seqlens"][-1])
     ms = ev_ms
@@ -228,7 +221,8 @@ def main():
         "effective_tflops": round(eff_tflops, 2),
         "effective_frac_of_peak": round(eff_tflops / PEAK_BF16_TFLOPS, 4),
         "pair_level_tflops": round(pair_tflops, 2),
-        "computed_tiles": tiles,
+        "computed_tiles": head_tiles,
+        "tile_list_entries": tiles,
         "attended_pairs": pairs,
         "all_fa_ms_per_layer": None if allfa_ms is None else round(allfa_ms, 4),
         "speedup_vs_all_fa": None if speedup is None else round(speedup, 4),

@@ -33,6 +33,8 @@ static ea_status make_dims(const ea_attn_desc* desc, EaDims* d) {
   d->Hq = a.num_q_heads;
   d->Hkv = a.num_kv_heads;
   d->G = a.num_q_heads / a.num_kv_heads;
+  d->hpw = (d->G % 2 == 0) ? 2 : 1;
+  d->ngr = d->G / d->hpw;
   d->D = a.head_dim;
   d->B = a.block;
   d->S = a.xa_stride;

@@ -17,6 +17,8 @@ namespace ea {
 // data (cu_seqlens lives on the device).
 struct EaDims {
   int32_t nseq, T, maxL, Hq, Hkv, G, D, B, S, r;  // r = B / S reduced rows per block
+  int32_t hpw;      // q-heads per attention workgroup (2 when G is even, else 1)
+  int32_t ngr;      // head groups per KV head: G / hpw
   float scale;
   int32_t sink, window, tau_num, tau_den;
   int64_t nqb_max;  // bound on sum_b ceil(L_b / B):  T / B + nseq
@@ -41,6 +43,8 @@ enum {
   SCAL_XA_PAIRS = 1,  // number of XA (sequence, q-head) pairs that score
   SCAL_N_UNITS = 3,   // total_qb * Hkv
   SCAL_CTR64 = 4,     // int64 work counter of the persistent scoring kernel (words 4..5)
+  SCAL_HEAD_TILES64 = 6,  // int64: (tile, q-head) pairs the attention computes (words 6..7)
+  SCAL_TILES64 = 8,       // int64: entries of the flat tile list (words 8..9)
   SCAL_COUNT = 16
 };
 
@@ -77,8 +81,12 @@ hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint16_t* 
 __host__ __device__ inline int64_t tri64(int64_t n) { return n * (n + 1) / 2; }
 __host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
-// Tile-list entry: kv-block index in the low 31 bits, bit 31 = needs a mask.
+// Tile-list entry: kv-block index in bits 0..28, bit 31 = needs a token mask,
+// bits 29 and 30 = the first / second q-head of the row's head group attends
+// this tile (XA heads of one group may select different blocks).
 constexpr uint32_t TILE_MASK_FLAG = 0x80000000u;
+constexpr uint32_t TILE_HEAD0 = 0x20000000u;
+constexpr uint32_t TILE_J_MASK = 0x1FFFFFFFu;
 
 // Sanitised mode byte: anything but SSA / XA runs as FA.
 __host__ __device__ inline int sane_mode(uint8_t m) {

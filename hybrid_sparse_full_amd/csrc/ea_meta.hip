@@ -60,8 +60,7 @@ __global__ __launch_bounds__(META_NT) void k_seq_meta(EaDims d, const int32_t* _
     m.scal[SCAL_TOTAL_QB] = (int32_t)totq;
     m.scal[SCAL_N_UNITS] = (int32_t)(totq * d.Hkv);
     m.scal[SCAL_XA_PAIRS] = 0;
-    m.scal[SCAL_CTR64] = 0;
-    m.scal[SCAL_CTR64 + 1] = 0;
+    for (int i = SCAL_CTR64; i < SCAL_COUNT; ++i) m.scal[i] = 0;
   }
   __syncthreads();
 

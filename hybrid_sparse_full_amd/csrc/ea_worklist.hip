@@ -4,9 +4,10 @@
 //   k_vt     V [T,Hkv,d] -> V^T [Hkv][d][padded tokens], keys permuted inside
 //            each 32-key group to match the MFMA operand order of the
 //            attention kernel, zero past the end of every sequence.
-//   k_cost   tiles per row (FA: I+1, SSA: sink + window blocks, XA: mask
-//            popcount); per unit (q-block, KV head) the max over its GQA
-//            siblings; histogram of unit costs.
+//   k_cost   tiles per row (FA: I+1, SSA: sink + window blocks, XA: popcount
+//            of the union of the group's mask rows); a row is a (q-block,
+//            group of 1 or 2 GQA sibling q-heads) that one workgroup serves;
+//            per unit (q-block, KV head) the max over its rows; histogram.
 //   k_sched  one workgroup: counting sort of units by cost, descending, and
 //            the exclusive scan of row costs (row offsets into the list).
 //   k_fill   one wave per row writes its kv-block indices, each flagged when
@@ -111,28 +112,37 @@ __global__ __launch_bounds__(256) void k_cost(EaDims d, const uint8_t* __restric
   const int g = (int)(u % d.Hkv);
   const RowInfo ri = decode_qb(d, m, qbg, g, modes, xa_mask);
   int32_t uc = 0;
-  for (int k = 0; k < d.G; ++k) {
-    const int h = g * d.G + k;
+  int64_t head_tiles = 0;
+  for (int kg = 0; kg < d.ngr; ++kg) {
     int32_t c;
     if (ri.mode == EA_MODE_SSA) {
       int32_t jlo, ns;
       ssa_ranges(d, ri.I, &jlo, &ns);
       c = ns + ri.I - jlo + 1;
+      head_tiles += (int64_t)c * d.hpw;
     } else if (ri.mode == EA_MODE_XA) {
-      const uint32_t* row = xa_mask + ((int64_t)qbg * d.Hq + h) * d.words;
+      // Union of the blocks selected by the heads of this group.
+      const uint32_t* row = xa_mask + ((int64_t)qbg * d.Hq + g * d.G + kg * d.hpw) * d.words;
       c = 0;
       for (int w = 0; w * 32 <= ri.I; ++w) {
-        uint32_t bits = row[w];
         const int hi = ri.I - w * 32;  // keep J <= I
-        if (hi < 31) bits &= (2u << hi) - 1u;
+        const uint32_t keep = hi < 31 ? (2u << hi) - 1u : 0xffffffffu;
+        uint32_t bits = 0;
+        for (int e = 0; e < d.hpw; ++e) {
+          const uint32_t be = row[(int64_t)e * d.words + w] & keep;
+          head_tiles += __popc(be);
+          bits |= be;
+        }
         c += __popc(bits);
       }
     } else {
       c = ri.I + 1;
+      head_tiles += (int64_t)c * d.hpw;
     }
-    row_cost[u * d.G + k] = c;
+    row_cost[u * d.ngr + kg] = c;
     uc = max(uc, c);
   }
+  atomicAdd((unsigned long long*)(m.scal + SCAL_HEAD_TILES64), (unsigned long long)head_tiles);
   unit_cost[u] = uc;
   atomicAdd(&hist[uc], 1);
 }
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
     sorted_units[pos] = u;
   }
   // Row offsets into the flat tile list (natural row order).
-  const int64_t nr = (int64_t)nu * d.G;
+  const int64_t nr = (int64_t)nu * d.ngr;
   const int64_t chunk = (nr + SCHED_NT - 1) / SCHED_NT;
   const int64_t r0 = min(nr, tid * chunk), r1 = min(nr, r0 + chunk);
   int64_t s = 0;
@@ -181,7 +191,10 @@ __global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
     row_off[r] = e;
     e += row_cost[r];
   }
-  if (tid == 0) row_off[nr] = tot;
+  if (tid == 0) {
+    row_off[nr] = tot;
+    *(int64_t*)(m.scal + SCAL_TILES64) = tot;
+  }
 }
 
 // ---------------------------------------------------------------- k_fill
@@ -192,28 +205,31 @@ __global__ __launch_bounds__(256) void k_fill(EaDims d, const uint8_t* __restric
                                               uint32_t* __restrict__ tiles) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= (int64_t)m.scal[SCAL_N_UNITS] * d.G) return;
-  const int64_t u = row / d.G;
-  const int k = (int)(row % d.G);
+  if (row >= (int64_t)m.scal[SCAL_N_UNITS] * d.ngr) return;
+  const int64_t u = row / d.ngr;
+  const int kg = (int)(row % d.ngr);
   const int32_t qbg = (int32_t)(u / d.Hkv);
   const int g = (int)(u % d.Hkv);
-  const int h = g * d.G + k;
+  const int h0 = g * d.G + kg * d.hpw;
   const RowInfo ri = decode_qb(d, m, qbg, g, modes, xa_mask);
   const int64_t off = row_off[row];
   const int32_t cnt = row_cost[row];
   uint32_t* out = tiles + off;
+  const uint32_t all_heads = d.hpw == 2 ? (TILE_HEAD0 | (TILE_HEAD0 << 1)) : TILE_HEAD0;
   if (ri.mode == EA_MODE_XA) {
-    const uint32_t* mrow = xa_mask + ((int64_t)qbg * d.Hq + h) * d.words;
+    const uint32_t* mrow = xa_mask + ((int64_t)qbg * d.Hq + h0) * d.words;
     const int nw = ri.I / 32 + 1;
     int32_t base = 0;
     for (int w0 = 0; w0 < nw; w0 += 64) {
       const int w = w0 + lane;
-      uint32_t bits = 0;
+      uint32_t b0 = 0, b1 = 0;
       if (w < nw) {
-        bits = mrow[w];
         const int hi = ri.I - w * 32;
-        if (hi < 31) bits &= (2u << hi) - 1u;
+        const uint32_t keep = hi < 31 ? (2u << hi) - 1u : 0xffffffffu;
+        b0 = mrow[w] & keep;
+        if (d.hpw == 2) b1 = mrow[d.words + w] & keep;
       }
+      uint32_t bits = b0 | b1;
       const int32_t pc = __popc(bits);
       const int32_t inc = wave_inclusive_sum(pc);
       int32_t pos = base + inc - pc;
@@ -221,7 +237,9 @@ __global__ __launch_bounds__(256) void k_fill(EaDims d, const uint8_t* __restric
         const int t = __ffs(bits) - 1;
         bits &= bits - 1;
         const int32_t J = w * 32 + t;
-        out[pos++] = (uint32_t)J | (tile_needs_mask(d, ri.mode, ri.I, J, ri.len) ? TILE_MASK_FLAG : 0u);
+        const uint32_t hb = (((b0 >> t) & 1u) ? TILE_HEAD0 : 0u) | (((b1 >> t) & 1u) ? (TILE_HEAD0 << 1) : 0u);
+        out[pos++] = (uint32_t)J | hb |
+                     (tile_needs_mask(d, ri.mode, ri.I, J, ri.len) ? TILE_MASK_FLAG : 0u);
       }
       base += __shfl(inc, 63, 64);
     }
@@ -233,7 +251,7 @@ __global__ __launch_bounds__(256) void k_fill(EaDims d, const uint8_t* __restric
     int32_t J;
     if (ri.mode == EA_MODE_SSA) J = t < ns ? t : jlo + (t - ns);
     else J = t;
-    out[t] = (uint32_t)J | (tile_needs_mask(d, ri.mode, ri.I, J, ri.len) ? TILE_MASK_FLAG : 0u);
+    out[t] = (uint32_t)J | all_heads | (tile_needs_mask(d, ri.mode, ri.I, J, ri.len) ? TILE_MASK_FLAG : 0u);
   }
 }
 
@@ -259,7 +277,7 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* v, const uint8_t* mo
                      xa_mask, m, unit_cost, row_cost, hist);
   hipLaunchKernelGGL(k_sched, dim3(1), dim3(SCHED_NT), 0, st, d, m, unit_cost, row_cost, hist,
                      cursor, sorted_units, row_off);
-  const int64_t rows = d.nqb_max * d.Hq;
+  const int64_t rows = d.nqb_max * d.Hkv * d.ngr;
   hipLaunchKernelGGL(k_fill, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, d, modes, xa_mask,
                      m, row_cost, row_off, tiles);
   return hipGetLastError();

@@ -67,6 +67,20 @@ __device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr
                : "memory", "m0");
 }
 
+// Scheduling pattern for an LDS-fed MFMA sequence of STEPS k-steps with N
+// independent accumulators: fragment reads run two k-steps ahead of the
+// MFMAs that consume them.
+template <int N, int STEPS>
+__device__ inline void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * N, 0);
+#pragma unroll
+  for (int i = 0; i < STEPS - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, N, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, N, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * N, 0);
+}
+
 __device__ inline uint32_t lds_region(uint32_t base, int R) {
   return __builtin_amdgcn_readfirstlane(base + (uint32_t)R * 1024u);
 }
@@ -198,21 +212,39 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   f32x16 sacc[C::NKT];
   bf16x8 pb[C::NKT][2];
 
-  // S^T = K Q^T for the B keys of the tile in K buffer `buf`.
+  // S^T = K Q^T for the B keys of the tile in K buffer `buf`.  k-step outer,
+  // sub-tile inner: consecutive MFMAs use independent accumulators, and the
+  // K fragments of the next k-step are read while the current ones multiply.
   auto compute_s = [&](int buf) {
     const uint16_t* Ks = smem + buf * C::TILE_ELEMS;
+    auto kfrag = [&](int kt, int s) {
+      const int kr = 32 * kt + l32;
+      return *(const bf16x8*)(Ks + kr * D + (((2 * s + half) ^ (kr & (C::KCH - 1))) * 8));
+    };
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
+    for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-      const int kr = 32 * kt + l32;
+    bf16x8 fa[C::NKT], fb[C::NKT];
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        const bf16x8 a =
-            *(const bf16x8*)(Ks + kr * D + (((2 * s + half) ^ (kr & (C::KCH - 1))) * 8));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+    for (int kt = 0; kt < C::NKT; ++kt) fa[kt] = kfrag(kt, 0);
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; s += 2) {
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt) fb[kt] = kfrag(kt, s + 1);
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kt], qf[s], sacc[kt], 0, 0, 0);
+      if (s + 2 < C::KSTEPS) {
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt) fa[kt] = kfrag(kt, s + 2);
       }
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kt], qf[s + 1], sacc[kt], 0, 0, 0);
     }
+    // Keep the reads one k-step ahead of the MFMAs that consume them.
+    sched_reads_ahead<C::NKT, C::KSTEPS>();
   };
 
   // Token mask (flagged tiles), online-softmax statistics and P = exp2(.) in bf16.
@@ -270,18 +302,33 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int r = 0; r < 16; ++r) oacc[tt][r] *= alpha;
     }
     const uint16_t* Vs = smem + (C::KBUF + buf) * C::TILE_ELEMS;
-#pragma unroll
-    for (int tt = 0; tt < C::NDT; ++tt) {
+    // k-step (16 keys) outer, d-tile inner: independent accumulators back to
+    // back, V^T fragments of the next k-step read ahead.
+    auto vfrag = [&](int tt, int ks) {
       const int dr = 32 * tt + l32;
+      const int ch = 2 * ks + half;  // = 4 kt + 2 mm + half with ks = 2 kt + mm
+      return *(const bf16x8*)(Vs + dr * B + ((ch ^ (dr & (C::VCH - 1))) * 8));
+    };
+    constexpr int KS = 2 * C::NKT;
+    bf16x8 fa[C::NDT], fb[C::NDT];
 #pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
+    for (int tt = 0; tt < C::NDT; ++tt) fa[tt] = vfrag(tt, 0);
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const int ch = 4 * kt + 2 * mm + half;
-          const bf16x8 a = *(const bf16x8*)(Vs + dr * B + ((ch ^ (dr & (C::VCH - 1))) * 8));
-          oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][mm], oacc[tt], 0, 0, 0);
-        }
+    for (int ks = 0; ks < KS; ks += 2) {
+#pragma unroll
+      for (int tt = 0; tt < C::NDT; ++tt) fb[tt] = vfrag(tt, ks + 1);
+#pragma unroll
+      for (int tt = 0; tt < C::NDT; ++tt)
+        oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tt], pb[ks >> 1][ks & 1], oacc[tt], 0, 0, 0);
+      if (ks + 2 < KS) {
+#pragma unroll
+        for (int tt = 0; tt < C::NDT; ++tt) fa[tt] = vfrag(tt, ks + 2);
+      }
+#pragma unroll
+      for (int tt = 0; tt < C::NDT; ++tt)
+        oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tt], pb[(ks + 1) >> 1][(ks + 1) & 1], oacc[tt], 0, 0, 0);
     }
+    sched_reads_ahead<C::NDT, KS>();
   };
 
   // Tile loop.  At the top of iteration t every wave waits for its own DMA of

@@ -78,7 +78,7 @@ size_t ws_layout(const EaDims& d, int op, WsLayout* L) {
   } else {
     const size_t units = (size_t)d.nqb_max * d.Hkv;
     const size_t rows = (size_t)d.nqb_max * d.Hq;
-    L->vt = take(2 * (size_t)d.Hkv * d.D * (size_t)d.tpad);
+    L->kvp = take(2 * 2 * (size_t)d.Hkv * d.D * (size_t)d.tpad);  // packed K, then V^T
     L->unit_cost = take(4 * units);
     L->row_cost = take(4 * rows);
     L->row_off = take(8 * (rows + 1));
@@ -141,7 +141,7 @@ int64_t ea_workspace_offset(const ea_attn_desc* desc, int op, const char* name) 
       {"qb_prefix", 0, L.qb_prefix},   {"tri_prefix", 0, L.tri_prefix},
       {"qb2seq", 0, L.qb2seq},         {"scal", 0, L.scal},
       {"xa_pair_bh", 1, L.xa_pair_bh}, {"xa_pair_items", 1, L.xa_pair_items},
-      {"xa_lse", 1, L.xa_lse},         {"vt", 2, L.vt},
+      {"xa_lse", 1, L.xa_lse},         {"kvp", 2, L.kvp},
       {"unit_cost", 2, L.unit_cost},   {"row_cost", 2, L.row_cost},
       {"row_off", 2, L.row_off},       {"hist", 2, L.hist},
       {"cursor", 2, L.cursor},         {"sorted_units", 2, L.sorted_units},
@@ -218,10 +218,10 @@ ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, co
   if (launch_seq_meta(d, cu_seqlens_dev, modes_dev, m, workspace_dev, L, false, nullptr, s) !=
       hipSuccess)
     return EA_ERR_HIP;
-  if (launch_worklist(d, (const uint16_t*)v_dev, modes_dev, xa_mask_dev, m, workspace_dev, L, s) !=
+  if (launch_worklist(d, (const uint16_t*)k_dev, (const uint16_t*)v_dev, modes_dev, xa_mask_dev, m, workspace_dev, L, s) !=
       hipSuccess)
     return EA_ERR_HIP;
-  if (launch_attention(d, (const uint16_t*)q_dev, (const uint16_t*)k_dev, modes_dev, m,
+  if (launch_attention(d, (const uint16_t*)q_dev, modes_dev, m,
                        workspace_dev, L, (uint16_t*)o_out_dev, lse_out_dev, s) != hipSuccess)
     return EA_ERR_HIP;
   return EA_OK;

@@ -59,12 +59,20 @@ struct AttnCfg {
 };
 
 // 16 bytes per lane from global memory (scalar base + 32-bit per-lane byte
-// offset) straight into LDS at m0 + 16 * lane.
+// offset) straight into LDS at m0 + 16 * lane.  No "memory" clobber: the LDS
+// slot written here is read only after the next workgroup barrier (whose asm
+// does carry one), so the scheduler may move LDS reads and MFMAs across it.
 __device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  // The base is wave-uniform by construction; readfirstlane states it.
+  // (readfirstlane returns int: widen through uint32_t, never sign-extend.)
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
+               : "v"(voff), "s"((const void*)(uintptr_t)bs), "s"(lds_addr)
+               : "m0");
 }
 
 // Scheduling pattern for an LDS-fed MFMA sequence of STEPS k-steps with N
@@ -94,8 +102,8 @@ __device__ inline void wait_vm_barrier() {
 
 template <int D, int B, int HPW>
 __global__ __launch_bounds__(HPW * (B / 32) * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-            const uint16_t* __restrict__ vt, const uint8_t* __restrict__ modes, SeqMeta m,
+void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
+            const uint16_t* __restrict__ vp, const uint8_t* __restrict__ modes, SeqMeta m,
             const int32_t* __restrict__ sorted_units, const int64_t* __restrict__ row_off,
             const int32_t* __restrict__ row_cost, const uint32_t* __restrict__ tiles,
             uint16_t* __restrict__ o, float* __restrict__ lse) {
@@ -151,8 +159,8 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   float alpha = 1.f;       // rescale of O still owed before the next PV
   bool rescale = false;
   const float C2 = d.scale * LOG2E;
-  const int64_t vrow0 = (int64_t)g * D * d.tpad;
-  const int64_t vkey0 = (int64_t)m.qb_prefix[b] * B;
+  // Packed tiles of this KV head: tile of kv block J at (g * nqb_max + P_b + J).
+  const int64_t tile0 = (int64_t)g * d.nqb_max + m.qb_prefix[b];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   // Token-mask limits of this lane: key j is allowed iff j <= jmax and
   // (j < jsink or j >= jwin).
@@ -160,52 +168,42 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int32_t jsink = mode == EA_MODE_SSA ? d.sink : 0x3fffffff;
   const int32_t jwin = qi - d.window + 1;
 
-  // LDS: K ring then V^T ring.  DMA region R (1 KB) of a tile holds rows
-  // R * RPR .. R * RPR + RPR - 1; lane l writes row R * RPR + l / CH, physical
-  // chunk l % CH, which holds logical chunk (l % CH) ^ (row % CH).  Row and
-  // chunk offsets split into a lane part (held in three registers) and a
-  // uniform part (folded into the scalar base); the swizzle's dependence on R
-  // is a uniform XOR.
+  // LDS: K ring then V^T ring.  Packed tiles are contiguous and zero padded.
+  // DMA region R (1 KB) of a tile holds rows R * RPR .. R * RPR + RPR - 1;
+  // lane l writes row R * RPR + l / CH, physical chunk l % CH, which must
+  // hold logical chunk (l % CH) ^ (row % CH).  The byte offset in the tile is
+  // R * 1024 (uniform, into the scalar base) + (lk ^ xr(R)) with a lane
+  // constant lk and a uniform XOR xr(R).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t krowb = (uint32_t)(d.Hkv * D * 2);  // bytes between K tokens
-  const uint32_t vrowb = (uint32_t)(d.tpad * 2);      // bytes between V^T rows
-  const uint32_t kc16 = (uint32_t)(((lane % C::KCH) ^ (lane / C::KCH)) * 16);
-  const uint32_t klane = (uint32_t)(lane / C::KCH) * krowb;
-  const uint32_t vc16 = (uint32_t)(((lane % C::VCH) ^ (lane / C::VCH)) * 16);
-  const uint32_t vlane = (uint32_t)(lane / C::VCH) * vrowb;
-  auto issue_k = [&](int buf, int32_t J) {
-    const uint32_t lbase = lds0 + (uint32_t)buf * C::TILE_BYTES;
-    const int64_t ktok0 = tok0 + (int64_t)J * B;
-    const char* kb = (const char*)(k + (ktok0 * d.Hkv + g) * D);
-    if (ktok0 + B <= (int64_t)d.T) {
-      // Rows past the sequence end read the next tokens of the buffer; the
-      // tile is flagged and those keys are masked.
-#pragma unroll
-      for (int i = 0; i < C::NI_K; ++i) {
-        const int R = wv * C::NI_K + i;
-        const uint32_t xr = C::RPR_K < C::KCH ? (uint32_t)(C::RPR_K * (R % (C::KCH / C::RPR_K)) * 16) : 0u;
-        dma16(kb + (size_t)R * C::RPR_K * krowb, klane + (kc16 ^ xr), lds_region(lbase, R));
-      }
-    } else {
-      // Tile reaches past the token buffer: clamp rows to the last token.
-#pragma unroll
-      for (int i = 0; i < C::NI_K; ++i) {
-        const int R = wv * C::NI_K + i;
-        const int r = R * C::RPR_K + lane / C::KCH;
-        const int rc = (int)min<int64_t>(r, (int64_t)d.T - 1 - ktok0);
-        const int c = (lane % C::KCH) ^ (r & (C::KCH - 1));
-        dma16(kb, (uint32_t)rc * krowb + (uint32_t)c * 16u, lds_region(lbase, R));
-      }
-    }
+  const uint32_t lk = (uint32_t)((lane / C::KCH) * (D * 2) + 16 * ((lane % C::KCH) ^ (lane / C::KCH)));
+  const uint32_t lv = (uint32_t)((lane / C::VCH) * (B * 2) + 16 * ((lane % C::VCH) ^ (lane / C::VCH)));
+  // DMA instruction i (0 <= i < NI_K) of this wave for the K tile of block
+  // J into K ring slot `buf` (resp. the V^T tile into V ring slot `buf`).
+  auto dma_k = [&](int buf, int32_t J, int i) {
+    const int R = wv * C::NI_K + i;
+    const uint32_t xr = C::RPR_K < C::KCH ? (uint32_t)(C::RPR_K * (R % (C::KCH / C::RPR_K)) * 16) : 0u;
+    const char* src = (const char*)(kp + (tile0 + J) * C::TILE_ELEMS) + R * 1024;
+    dma16(src, lk ^ xr, lds_region(lds0 + (uint32_t)buf * C::TILE_BYTES, R));
   };
-  auto issue_v = [&](int buf, int32_t J) {
-    const uint32_t lbase = lds0 + (uint32_t)(C::KBUF + buf) * C::TILE_BYTES;
-    const char* vb = (const char*)(vt + vrow0 + vkey0 + (int64_t)J * B);
+  auto dma_v = [&](int buf, int32_t J, int i) {
+    const int R = wv * C::NI_K + i;
+    const uint32_t xr = C::RPR_V < C::VCH ? (uint32_t)(C::RPR_V * (R % (C::VCH / C::RPR_V)) * 16) : 0u;
+    const char* src = (const char*)(vp + (tile0 + J) * C::TILE_ELEMS) + R * 1024;
+    dma16(src, lv ^ xr, lds_region(lds0 + (uint32_t)(C::KBUF + buf) * C::TILE_BYTES, R));
+  };
+
+  // The 2 * NI_K DMA instructions of this wave for the next tile, spread
+  // over the `n` MFMA double-steps of one compute phase: at double-step j,
+  // issue the instructions with index in [j * per, (j + 1) * per).
+  int nk = 0, nv = 0;  // ring slots of the next tile (set per iteration)
+  auto dma_slot = [&](int j, int n, int32_t dJ) {
+    constexpr int TOT = 2 * C::NI_K;
+    const int per = (TOT + n - 1) / n;
 #pragma unroll
-    for (int i = 0; i < C::NI_K; ++i) {
-      const int R = wv * C::NI_K + i;
-      const uint32_t xr = C::RPR_V < C::VCH ? (uint32_t)(C::RPR_V * (R % (C::VCH / C::RPR_V)) * 16) : 0u;
-      dma16(vb + (size_t)R * C::RPR_V * vrowb, vlane + (vc16 ^ xr), lds_region(lbase, R));
+    for (int x = 0; x < per; ++x) {
+      const int idx = j * per + x;
+      if (idx < C::NI_K) dma_k(nk, dJ, idx);
+      else if (idx < TOT) dma_v(nv, dJ, idx - C::NI_K);
     }
   };
 
@@ -213,9 +211,11 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   bf16x8 pb[C::NKT][2];
 
   // S^T = K Q^T for the B keys of the tile in K buffer `buf`.  k-step outer,
-  // sub-tile inner: consecutive MFMAs use independent accumulators, and the
-  // K fragments of the next k-step are read while the current ones multiply.
-  auto compute_s = [&](int buf) {
+  // sub-tile inner: consecutive MFMAs use independent accumulators and the K
+  // fragments are read two k-steps ahead.  If `dJ` >= 0, this wave's DMA
+  // instructions for the next K tile (block dJ, ring slot `dbuf`) are spread
+  // between the MFMA groups, so their issue stalls overlap running MFMAs.
+  auto compute_s = [&](int buf, int32_t dJ) {
     const uint16_t* Ks = smem + buf * C::TILE_ELEMS;
     auto kfrag = [&](int kt, int s) {
       const int kr = 32 * kt + l32;
@@ -229,9 +229,9 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) fa[kt] = kfrag(kt, 0);
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; s += 2) {
+    for (int kt = 0; kt < C::NKT; ++kt) fb[kt] = kfrag(kt, 1);
 #pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt) fb[kt] = kfrag(kt, s + 1);
+    for (int s = 0; s < C::KSTEPS; s += 2) {
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kt], qf[s], sacc[kt], 0, 0, 0);
@@ -242,9 +242,12 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kt], qf[s + 1], sacc[kt], 0, 0, 0);
+      if (s + 3 < C::KSTEPS) {
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt) fb[kt] = kfrag(kt, s + 3);
+      }
+      if (dJ >= 0) dma_slot(s / 2, C::KSTEPS / 2, dJ);
     }
-    // Keep the reads one k-step ahead of the MFMAs that consume them.
-    sched_reads_ahead<C::NKT, C::KSTEPS>();
   };
 
   // Token mask (flagged tiles), online-softmax statistics and P = exp2(.) in bf16.
@@ -293,8 +296,11 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
     lrun = (rescale ? lrun * alpha : lrun) + psum;
   };
 
-  // O^T += V^T P^T with the V^T tile in buffer `buf` (after the owed rescale).
-  auto compute_pv = [&](int buf) {
+  // O^T += V^T P^T with the V^T tile in buffer `buf` (after the owed
+  // rescale); k-step (16 keys) outer, d-tile inner, V^T fragments two k-steps
+  // ahead, and this wave's DMA of the next V^T tile (if dJ >= 0) spread
+  // between the MFMA groups.
+  auto compute_pv = [&](int buf, int32_t dJ) {
     if (rescale) {
 #pragma unroll
       for (int tt = 0; tt < C::NDT; ++tt)
@@ -302,8 +308,6 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int r = 0; r < 16; ++r) oacc[tt][r] *= alpha;
     }
     const uint16_t* Vs = smem + (C::KBUF + buf) * C::TILE_ELEMS;
-    // k-step (16 keys) outer, d-tile inner: independent accumulators back to
-    // back, V^T fragments of the next k-step read ahead.
     auto vfrag = [&](int tt, int ks) {
       const int dr = 32 * tt + l32;
       const int ch = 2 * ks + half;  // = 4 kt + 2 mm + half with ks = 2 kt + mm
@@ -314,9 +318,9 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
     for (int tt = 0; tt < C::NDT; ++tt) fa[tt] = vfrag(tt, 0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ks += 2) {
+    for (int tt = 0; tt < C::NDT; ++tt) fb[tt] = vfrag(tt, 1);
 #pragma unroll
-      for (int tt = 0; tt < C::NDT; ++tt) fb[tt] = vfrag(tt, ks + 1);
+    for (int ks = 0; ks < KS; ks += 2) {
 #pragma unroll
       for (int tt = 0; tt < C::NDT; ++tt)
         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tt], pb[ks >> 1][ks & 1], oacc[tt], 0, 0, 0);
@@ -327,49 +331,74 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
       for (int tt = 0; tt < C::NDT; ++tt)
         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tt], pb[(ks + 1) >> 1][(ks + 1) & 1], oacc[tt], 0, 0, 0);
+      if (ks + 3 < KS) {
+#pragma unroll
+        for (int tt = 0; tt < C::NDT; ++tt) fb[tt] = vfrag(tt, ks + 3);
+      }
+      if (dJ >= 0) dma_slot(ks / 2, KS / 2, dJ);
     }
-    sched_reads_ahead<C::NDT, KS>();
   };
 
   // Tile loop.  At the top of iteration t every wave waits for its own DMA of
-  // tile t and joins the barrier; then K(t+1) and V(t+1) are issued into the
-  // ring slots freed by iteration t-1 and stream in while tile t is computed.
-  // Head 0 of the group runs S(t) -> softmax(t) -> PV(t); head 1 runs
-  // PV(t-1) -> S(t) -> softmax(t), half a tile behind.  Each SIMD holds one
-  // wave of each head, so the softmax of one overlaps the MFMAs of the other.
+  // tile t and joins the barrier; the DMA of K(t+1) and V(t+1) into the ring
+  // slots freed by iteration t-1 is issued from inside the S and PV MFMA
+  // sequences of iteration t.  Head 0 of the group runs S(t) -> softmax(t) ->
+  // PV(t); head 1 runs PV(t-1) -> S(t) -> softmax(t), half a tile behind, so
+  // on each SIMD the softmax of one wave overlaps the MFMAs of the other.
   const bool lag = HPW == 2 && hsub == 1;
   bool pending = false;  // lagging head: P of the previous tile awaits its PV
   int pend_vbuf = 0;
   if (cnt > 0) {
     uint32_t ecur = tiles[off];
-    issue_k(0, (int32_t)(ecur & TILE_J_MASK));
-    issue_v(0, (int32_t)(ecur & TILE_J_MASK));
+#pragma unroll
+    for (int i = 0; i < C::NI_K; ++i) dma_k(0, (int32_t)(ecur & TILE_J_MASK), i);
+#pragma unroll
+    for (int i = 0; i < C::NI_K; ++i) dma_v(0, (int32_t)(ecur & TILE_J_MASK), i);
     for (int t = 0; t < cnt; ++t) {
       const uint32_t enext = t + 1 < cnt ? tiles[off + t + 1] : 0u;
       wait_vm_barrier<0>();
-      if (t + 1 < cnt) {
-        issue_k((t + 1) % C::KBUF, (int32_t)(enext & TILE_J_MASK));
-        issue_v((t + 1) % C::VBUF, (int32_t)(enext & TILE_J_MASK));
-      }
+      const int32_t nJ = t + 1 < cnt ? (int32_t)(enext & TILE_J_MASK) : -1;
+      nk = (t + 1) % C::KBUF;
+      nv = (t + 1) % C::VBUF;
       const bool mine = (ecur & mybit) != 0;
+      // Each wave issues its whole DMA share of tile t+1 from the first MFMA
+      // phase it runs in this iteration, so the data has most of the tile
+      // to land before the next barrier.
+      bool issued = false;
       if (!lag) {
         if (mine) {
-          compute_s(t % C::KBUF);
+          compute_s(t % C::KBUF, nJ);
+          issued = true;
           softmax(ecur);
-          compute_pv(t % C::VBUF);
+          compute_pv(t % C::VBUF, -1);
         }
       } else {
-        if (pending) compute_pv(pend_vbuf);
+        if (pending) {
+          compute_pv(pend_vbuf, nJ);
+          issued = true;
+        }
         if (mine) {
-          compute_s(t % C::KBUF);
+          // Win the matrix core over head 0's PV for this S, so the SIMD runs
+          // h0.S, h1.PV, h1.S, h0.PV back to back with both softmaxes hidden.
+          __builtin_amdgcn_s_setprio(1);
+          compute_s(t % C::KBUF, issued ? -1 : nJ);
+          __builtin_amdgcn_s_setprio(0);
+          issued = issued || nJ >= 0;
           softmax(ecur);
         }
         pending = mine;
         pend_vbuf = t % C::VBUF;
       }
+      // A wave with no MFMA phase this iteration still issues its share.
+      if (nJ >= 0 && !issued) {
+#pragma unroll
+        for (int i = 0; i < C::NI_K; ++i) dma_k(nk, nJ, i);
+#pragma unroll
+        for (int i = 0; i < C::NI_K; ++i) dma_v(nv, nJ, i);
+      }
       ecur = enext;
     }
-    if (pending) compute_pv(pend_vbuf);
+    if (pending) compute_pv(pend_vbuf, -1);
   }
 
   const float ltot = lrun + __shfl_xor(lrun, 32, 64);
@@ -392,11 +421,12 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
 }
 
-hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint16_t* k,
-                            const uint8_t* modes, const SeqMeta& m, void* ws, const WsLayout& L,
-                            uint16_t* o, float* lse, hipStream_t st) {
+hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint8_t* modes,
+                            const SeqMeta& m, void* ws, const WsLayout& L, uint16_t* o, float* lse,
+                            hipStream_t st) {
   char* w = (char*)ws;
-  const uint16_t* vt = (const uint16_t*)(w + L.vt);
+  const uint16_t* kp = (const uint16_t*)(w + L.kvp);
+  const uint16_t* vp = kp + (size_t)d.Hkv * d.D * (size_t)d.tpad;
   const int32_t* sorted_units = (const int32_t*)(w + L.sorted_units);
   const int64_t* row_off = (const int64_t*)(w + L.row_off);
   const int32_t* row_cost = (const int32_t*)(w + L.row_cost);
@@ -405,7 +435,7 @@ hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint16_t* 
   const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * d.ngr);
 #define EA_ATTN(DD, BB, HH)                                                                     \
   hipLaunchKernelGGL((k_attn<DD, BB, HH>), dim3(grid), dim3(AttnCfg<DD, BB, HH>::NT), 0, st, d, \
-                     q, k, vt, modes, m, sorted_units, row_off, row_cost, tiles, o, lse)
+                     q, kp, vp, modes, m, sorted_units, row_off, row_cost, tiles, o, lse)
   if (d.hpw == 2) {
     if (d.D == 128 && d.B == 128) EA_ATTN(128, 128, 2);
     else if (d.D == 128 && d.B == 64) EA_ATTN(128, 64, 2);

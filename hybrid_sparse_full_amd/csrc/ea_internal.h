@@ -24,7 +24,7 @@ struct EaDims {
   int64_t nqb_max;  // bound on sum_b ceil(L_b / B):  T / B + nseq
   int32_t maxqb;    // ceil(maxL / B): bound on q-blocks (and kv-blocks) per sequence
   int32_t words;    // ceil(maxqb / 32): uint32 words per mask row
-  int64_t tpad;     // nqb_max * B: padded token count of the transposed V
+  int64_t tpad;     // nqb_max * B: padded token count of the packed K / V^T tiles
   int64_t tri_max;  // bound on sum_b nQB_b (nQB_b + 1) / 2
 };
 
@@ -54,7 +54,7 @@ struct WsLayout {
   // XA select
   size_t xa_pair_bh, xa_pair_items, xa_lse;
   // prefill
-  size_t vt, unit_cost, row_cost, row_off, hist, cursor, sorted_units, tiles;
+  size_t kvp, unit_cost, row_cost, row_off, hist, cursor, sorted_units, tiles;
   size_t total;
 };
 
@@ -70,11 +70,10 @@ hipError_t launch_xa_score(const EaDims& d, const uint16_t* q, const uint16_t* k
 hipError_t launch_xa_select(const EaDims& d, const uint8_t* modes, const SeqMeta& m, void* ws,
                             const WsLayout& L, uint32_t* mask, int32_t* row_count,
                             int64_t* xa_pairs, float* block_mass, hipStream_t st);
-hipError_t launch_worklist(const EaDims& d, const uint16_t* v, const uint8_t* modes,
+hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v, const uint8_t* modes,
                            const uint32_t* xa_mask, const SeqMeta& m, void* ws,
                            const WsLayout& L, hipStream_t st);
-hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint16_t* k,
-                            const uint8_t* modes, const SeqMeta& m, void* ws,
+hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint8_t* modes, const SeqMeta& m, void* ws,
                             const WsLayout& L, uint16_t* o, float* lse, hipStream_t st);
 
 // ---- helpers usable on host and device ----

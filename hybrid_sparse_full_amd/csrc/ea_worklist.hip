@@ -1,9 +1,10 @@
 // Work-list builder of the fused prefill: one flat list of kv tiles for
 // every (q-block, q-head) row of every mode, plus a longest-first schedule.
 //
-//   k_vt     V [T,Hkv,d] -> V^T [Hkv][d][padded tokens], keys permuted inside
-//            each 32-key group to match the MFMA operand order of the
-//            attention kernel, zero past the end of every sequence.
+//   k_pack   K and V -> contiguous zero-padded tiles per (KV head, q-block):
+//            K key-major, V transposed (V^T) with keys permuted inside each
+//            32-key group to match the MFMA operand order of the attention
+//            kernel.
 //   k_cost   tiles per row (FA: I+1, SSA: sink + window blocks, XA: popcount
 //            of the union of the group's mask rows); a row is a (q-block,
 //            group of 1 or 2 GQA sibling q-heads) that one workgroup serves;
@@ -60,10 +61,14 @@ __device__ inline int swap_bits23(int p) {
   return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
 
-// ---------------------------------------------------------------- k_vt
+// ---------------------------------------------------------------- k_pack
+// Packs the K and V tiles of every (KV head g, global q-block qbg) into
+// contiguous, zero-padded B x d blocks: Kp[g][qbg] = K rows (key-major) and
+// Vp[g][qbg] = V^T (d-major, keys permuted inside each 32-key group).
 template <int D, int B>
-__global__ __launch_bounds__(256) void k_vt(EaDims d, const uint16_t* __restrict__ v, SeqMeta m,
-                                            uint16_t* __restrict__ vt) {
+__global__ __launch_bounds__(256) void k_pack(EaDims d, const uint16_t* __restrict__ k,
+                                              const uint16_t* __restrict__ v, SeqMeta m,
+                                              uint16_t* __restrict__ kp, uint16_t* __restrict__ vp) {
   __shared__ uint16_t tile[B][D + 2];
   const int32_t qbg = blockIdx.x;
   if (qbg >= m.scal[SCAL_TOTAL_QB]) return;
@@ -73,19 +78,23 @@ __global__ __launch_bounds__(256) void k_vt(EaDims d, const uint16_t* __restrict
   const int32_t len = m.len[b];
   const int64_t tok0 = (int64_t)m.start[b] + (int64_t)J * B;
   const int32_t nvalid = min(B, len - J * B);
-  // Load rows (keys) as 16-byte chunks.
-  constexpr int CPR = D / 8;  // chunks per row
+  const int64_t tile_off = ((int64_t)g * d.nqb_max + qbg) * (B * D);
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
   for (int c = threadIdx.x; c < B * CPR; c += 256) {
     const int key = c / CPR, ch = c % CPR;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < nvalid)
-      val = *(const uint4*)(v + ((tok0 + key) * d.Hkv + g) * D + ch * 8);
-    const uint16_t* pv = (const uint16_t*)&val;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (key < nvalid) {
+      const int64_t src = ((tok0 + key) * d.Hkv + g) * D + ch * 8;
+      kv = *(const uint4*)(k + src);
+      vv = *(const uint4*)(v + src);
+    }
+    *(uint4*)(kp + tile_off + key * D + ch * 8) = kv;
+    const uint16_t* pv = (const uint16_t*)&vv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) tile[key][ch * 8 + e] = pv[e];
   }
   __syncthreads();
-  // Write V^T rows: 8 consecutive (permuted) key positions per thread.
+  // V^T rows: 8 consecutive (permuted) key positions per thread.
   constexpr int CPD = B / 8;
   for (int c = threadIdx.x; c < D * CPD; c += 256) {
     const int dd = c / CPD, p0 = (c % CPD) * 8;
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(256) void k_vt(EaDims d, const uint16_t* __restrict
       const int key = (p & ~31) | swap_bits23(p & 31);
       outv[e] = tile[key][dd];
     }
-    *(uint4*)(vt + ((int64_t)g * D + dd) * d.tpad + (int64_t)qbg * B + p0) = *(const uint4*)outv;
+    *(uint4*)(vp + tile_off + dd * B + p0) = *(const uint4*)outv;
   }
 }
 
@@ -255,11 +264,12 @@ __global__ __launch_bounds__(256) void k_fill(EaDims d, const uint8_t* __restric
   }
 }
 
-hipError_t launch_worklist(const EaDims& d, const uint16_t* v, const uint8_t* modes,
+hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v, const uint8_t* modes,
                            const uint32_t* xa_mask, const SeqMeta& m, void* ws, const WsLayout& L,
                            hipStream_t st) {
   char* w = (char*)ws;
-  uint16_t* vt = (uint16_t*)(w + L.vt);
+  uint16_t* kp = (uint16_t*)(w + L.kvp);
+  uint16_t* vp = kp + (size_t)d.Hkv * d.D * (size_t)d.tpad;
   int32_t* unit_cost = (int32_t*)(w + L.unit_cost);
   int32_t* row_cost = (int32_t*)(w + L.row_cost);
   int64_t* row_off = (int64_t*)(w + L.row_off);
@@ -267,11 +277,13 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* v, const uint8_t* mo
   int32_t* cursor = (int32_t*)(w + L.cursor);
   int32_t* sorted_units = (int32_t*)(w + L.sorted_units);
   uint32_t* tiles = (uint32_t*)(w + L.tiles);
-  const dim3 gvt((unsigned)d.nqb_max, (unsigned)d.Hkv);
-  if (d.D == 128 && d.B == 128) hipLaunchKernelGGL((k_vt<128, 128>), gvt, dim3(256), 0, st, d, v, m, vt);
-  else if (d.D == 128 && d.B == 64) hipLaunchKernelGGL((k_vt<128, 64>), gvt, dim3(256), 0, st, d, v, m, vt);
-  else if (d.D == 64 && d.B == 128) hipLaunchKernelGGL((k_vt<64, 128>), gvt, dim3(256), 0, st, d, v, m, vt);
-  else hipLaunchKernelGGL((k_vt<64, 64>), gvt, dim3(256), 0, st, d, v, m, vt);
+  const dim3 gp((unsigned)d.nqb_max, (unsigned)d.Hkv);
+#define EA_PACK(DD, BB) hipLaunchKernelGGL((k_pack<DD, BB>), gp, dim3(256), 0, st, d, k, v, m, kp, vp)
+  if (d.D == 128 && d.B == 128) EA_PACK(128, 128);
+  else if (d.D == 128 && d.B == 64) EA_PACK(128, 64);
+  else if (d.D == 64 && d.B == 128) EA_PACK(64, 128);
+  else EA_PACK(64, 64);
+#undef EA_PACK
   const int64_t units = d.nqb_max * d.Hkv;
   hipLaunchKernelGGL(k_cost, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, d, modes,
                      xa_mask, m, unit_cost, row_cost, hist);

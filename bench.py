@@ -38,7 +38,91 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-fa", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output under DIR "
+                         "(subfolders fetch, write, cfetch, cwrite) into the traffic record")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of exactly 1 GiB, so that HBM byte counters read under the
+    same profiler can be scaled to bytes (read 1 GiB, write 1 GiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def _counter_means(folder, counter):
+    """Mean counter value (KiB per dispatch) per kernel name, from the
+    *_counter_collection.csv files rocprofv3 wrote under `folder`."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(folder, "**", "*_counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v)), len(v)) for k, v in vals.items()}
+
+
+def write_traffic(base, cfg_name):
+    """Scale the attention kernel's FETCH_SIZE / WRITE_SIZE by what the same
+    counters read for a 1 GiB device copy (bytes known), and store the result
+    keyed to the hash of the attention source it was measured on."""
+    import hashlib
+    def pick(d, key):
+        m = [v for k, v in d.items() if key in k]
+        if not m:
+            raise SystemExit(f"no dispatch of {key} in the counter output")
+        return m[0]
+    fetch = pick(_counter_means(os.path.join(base, "fetch"), "FETCH_SIZE"), "k_attn")
+    write = pick(_counter_means(os.path.join(base, "write"), "WRITE_SIZE"), "k_attn")
+    cf = pick(_counter_means(os.path.join(base, "cfetch"), "FETCH_SIZE"), "copyBuffer")
+    cw = pick(_counter_means(os.path.join(base, "cwrite"), "WRITE_SIZE"), "copyBuffer")
+    one_gib = float(1 << 30)
+    f_scale = one_gib / (cf[0] * 1024.0)
+    w_scale = one_gib / (cw[0] * 1024.0)
+    read_b = fetch[0] * 1024.0 * f_scale
+    write_b = write[0] * 1024.0 * w_scale
+    src = os.path.join(ROOT, "hybrid_sparse_full_amd", "csrc", "ea_attn.hip")
+    rec = {
+        "kernel": "k_attn", "workload": cfg_name,
+        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "fetch_kib_per_dispatch": round(fetch[0], 1), "fetch_dispatches": fetch[1],
+        "write_kib_per_dispatch": round(write[0], 1), "write_dispatches": write[1],
+        "copy_fetch_kib_per_GiB": round(cf[0], 1), "copy_write_kib_per_GiB": round(cw[0], 1),
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "read_bytes_per_launch": round(read_b), "write_bytes_per_launch": round(write_b),
+        "bytes_per_launch": round(read_b + write_b),
+    }
+    path = os.path.join(ROOT, "profiles", f"k_attn_{cfg_name}_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
+def traffic_record(cfg_name):
+    """Measured HBM bytes per attention launch, if a counter summary for the
+    current attention source exists under profiles/ (null otherwise)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_attn_{cfg_name}_traffic.json")
+    src = os.path.join(ROOT, "hybrid_sparse_full_amd", "csrc", "ea_attn.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
 
 
 def attended_pairs(inp, gpu_xa_pairs=None):
@@ -145,6 +229,12 @@ def cpu_baseline(inp, seconds):
 
 def main():
     a = parse()
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
+    if a.traffic_from:
+        write_traffic(a.traffic_from, a.config)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
                                    "design note, not an implemented path", "n_gpus": a.gpus}))
@@ -182,6 +272,7 @@ def main():
     pair_tflops = pair_flops / (ms * 1e-3) / 1e12
     attn_pair_tflops = pair_flops / (attn_ms * 1e-3) / 1e12
     rat = layer.ratios(cfg.sparse_mode)
+    traffic = traffic_record(cfg.name)
 
     speedup = None
     allfa_ms = None
@@ -237,7 +328,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_pair_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "per_launch_ms": round(attn_ms, 4),
             "algorithmic_flops_per_launch": pair_flops,
         },

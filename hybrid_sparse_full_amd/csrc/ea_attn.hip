@@ -9,13 +9,15 @@
 // different blocks; the list holds their union and a wave skips the tiles
 // that its head does not attend.
 //
-// Staging: LDS rings of two K tiles and three V^T tiles (160 KB for
-// B = d = 128), filled by global->LDS DMA (global_load_lds_dwordx4) one tile
-// ahead; one barrier per tile orders the rings.  The two heads of a group run
-// half a tile apart (head 1 applies P V of tile t-1 before S of tile t), so
-// on every SIMD the softmax of one wave overlaps the MFMAs of the other.  The DMA is issued from inline
-// assembly and its completion is tracked by hand (s_waitcnt vmcnt), because
-// the compiler's own tracking of LDS DMA waits for every outstanding load.
+// Staging: LDS rings of two K tiles and two V^T tiles (128 KB for
+// B = d = 128), filled by global->LDS DMA (global_load_lds_dwordx4) one
+// period ahead; one barrier per tile orders the rings.  Every wave runs
+// PV(t-1) and S(t) on the matrix core and the softmax of tile t on the
+// vector ALU; the two heads of a group do so half a period apart, so on
+// every SIMD the softmax of one wave overlaps the MFMAs of the other.  The
+// DMA is issued from inline assembly and its completion is tracked by hand
+// (s_waitcnt vmcnt), because the compiler's own tracking of LDS DMA waits
+// for every outstanding load.
 // The LDS image of each tile row is XOR-swizzled in 16-byte chunks so that
 // the MFMA operand reads are free of bank conflicts.
 //
@@ -30,8 +32,11 @@
 //                 inside each 32-key group of V^T is permuted (bits 2 and 3 of
 //                 the key index swapped) when V is transposed, so the registers
 //                 of P^T line up with the MFMA K index with no data movement.
-// Softmax: exp2 with the scale c*log2(e) folded into one FMA; the running max
-// is shared by both half-waves; O is rescaled only when some max grows.
+// Softmax: exp2 with the scale c*log2(e) folded into one FMA; the reference
+// max is shared by both half-waves (v_permlane32_swap, no LDS) and moves only
+// when a row max exceeds it by more than 2^8 in the exp2 domain, so O and l
+// are rescaled rarely; P stays below 256, which bf16 and fp32 hold exactly
+// as well as values below 1.
 #include "ea_device.h"
 
 namespace ea {
@@ -53,8 +58,8 @@ struct AttnCfg {
   static constexpr int KSTEPS = D / 16;
   static constexpr int NKT = B / 32;               // 32-key sub-tiles per kv tile
   static constexpr int NDT = D / 32;               // 32-row d tiles of O^T
-  static constexpr int KBUF = 2;                   // K tiles resident: t, t+1
-  static constexpr int VBUF = HPW == 2 ? 3 : 2;    // V^T tiles: t-1 (lagging head), t, t+1
+  static constexpr int KBUF = 2;                   // K tiles resident: t (in use), t+1 (landing)
+  static constexpr int VBUF = 2;                   // V^T tiles: t-1 (in use), t (landing)
   static_assert(REGIONS % NW == 0, "DMA regions must split evenly over waves");
 };
 
@@ -127,8 +132,9 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int32_t len = m.len[b];
   const int64_t tok0 = m.start[b];
   const int mode = sane_mode(modes[(int64_t)b * d.Hkv + g]);
-  const int64_t off = row_off[row];
-  const int32_t cnt = row_cost[row];
+  // Row data is wave-uniform: keep it (and so every DMA address) in SGPRs.
+  const int64_t off = uniform64(row_off[row]);
+  const int32_t cnt = __builtin_amdgcn_readfirstlane(row_cost[row]);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
@@ -160,7 +166,7 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   bool rescale = false;
   const float C2 = d.scale * LOG2E;
   // Packed tiles of this KV head: tile of kv block J at (g * nqb_max + P_b + J).
-  const int64_t tile0 = (int64_t)g * d.nqb_max + m.qb_prefix[b];
+  const int64_t tile0 = uniform64((int64_t)g * d.nqb_max + m.qb_prefix[b]);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   // Token-mask limits of this lane: key j is allowed iff j <= jmax and
   // (j < jsink or j >= jwin).
@@ -192,18 +198,28 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
     dma16(src, lv ^ xr, lds_region(lds0 + (uint32_t)(C::KBUF + buf) * C::TILE_BYTES, R));
   };
 
-  // The 2 * NI_K DMA instructions of this wave for the next tile, spread
-  // over the `n` MFMA double-steps of one compute phase: at double-step j,
-  // issue the instructions with index in [j * per, (j + 1) * per).
-  int nk = 0, nv = 0;  // ring slots of the next tile (set per iteration)
-  auto dma_slot = [&](int j, int n, int32_t dJ) {
-    constexpr int TOT = 2 * C::NI_K;
-    const int per = (TOT + n - 1) / n;
+  // DMA of one period: this wave's NI_K instructions for the K tile of
+  // block jk (ring slot nk) and its NI_K for the V^T tile of block jv (ring
+  // slot nv); a block of -1 means nothing to load.  A compute phase of n
+  // steps issues, at step j, the instructions with index in
+  // [j * per, (j + 1) * per), per = ceil(NI_K / n), so their issue overlaps
+  // the phase's MFMAs or exponentials.
+  int32_t jk = -1, jv = -1;
+  int nk = 0, nv = 0;
+  auto dma_k_part = [&](int j, int n) {
+    const int per = (C::NI_K + n - 1) / n;
 #pragma unroll
     for (int x = 0; x < per; ++x) {
       const int idx = j * per + x;
-      if (idx < C::NI_K) dma_k(nk, dJ, idx);
-      else if (idx < TOT) dma_v(nv, dJ, idx - C::NI_K);
+      if (idx < C::NI_K && jk >= 0) dma_k(nk, jk, idx);
+    }
+  };
+  auto dma_v_part = [&](int j, int n) {
+    const int per = (C::NI_K + n - 1) / n;
+#pragma unroll
+    for (int x = 0; x < per; ++x) {
+      const int idx = j * per + x;
+      if (idx < C::NI_K && jv >= 0) dma_v(nv, jv, idx);
     }
   };
 
@@ -212,10 +228,9 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   // S^T = K Q^T for the B keys of the tile in K buffer `buf`.  k-step outer,
   // sub-tile inner: consecutive MFMAs use independent accumulators and the K
-  // fragments are read two k-steps ahead.  If `dJ` >= 0, this wave's DMA
-  // instructions for the next K tile (block dJ, ring slot `dbuf`) are spread
-  // between the MFMA groups, so their issue stalls overlap running MFMAs.
-  auto compute_s = [&](int buf, int32_t dJ) {
+  // fragments are read two k-steps ahead.  With `dma`, this wave's share of
+  // the period's V^T DMA is spread between the MFMA groups.
+  auto compute_s = [&](int buf, bool dma) __attribute__((always_inline)) {
     const uint16_t* Ks = smem + buf * C::TILE_ELEMS;
     auto kfrag = [&](int kt, int s) {
       const int kr = 32 * kt + l32;
@@ -246,12 +261,14 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt) fb[kt] = kfrag(kt, s + 3);
       }
-      if (dJ >= 0) dma_slot(s / 2, C::KSTEPS / 2, dJ);
+      if (dma) dma_v_part(s / 2, C::KSTEPS / 2);
     }
   };
 
-  // Token mask (flagged tiles), online-softmax statistics and P = exp2(.) in bf16.
-  auto softmax = [&](uint32_t e) {
+  // Token mask (flagged tiles), online-softmax statistics and P = exp2(.) in
+  // bf16.  With `dma`, this wave's whole DMA share of the period is issued
+  // between the exponentials of the NKT sub-tiles.
+  auto softmax = [&](uint32_t e, bool dma) __attribute__((always_inline)) {
     if (__builtin_expect((e & TILE_MASK_FLAG) != 0, 0)) {
       // A real branch: only flagged tiles pay for the token mask.
       asm volatile("");
@@ -271,13 +288,18 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrun, mx);
-    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    rescale = __any(mnew > mrun);
-    alpha = __builtin_amdgcn_exp2f((mrun - mref) * C2);
-    mrun = mnew;
-    const float mb = mref * C2;
+    mx = halves_max(mx);
+    // The reference max mrun moves only when some row max of the wave
+    // exceeds it by more than 2^8 in the exp2 domain (or is its first finite
+    // value); otherwise P = exp2(c (s - mrun)) stays below 256 and neither O
+    // nor l needs rescaling.  l and O always refer to the same mrun.
+    rescale = __any((mx - mrun) * C2 > 8.0f);
+    if (rescale) {
+      const float mnew = fmaxf(mrun, mx);
+      alpha = __builtin_amdgcn_exp2f((mrun - ((mnew == -INFINITY) ? 0.f : mnew)) * C2);
+      mrun = mnew;
+    }
+    const float mb = ((mrun == -INFINITY) ? 0.f : mrun) * C2;
     // Row sum in fp32 (the bf16 copy of P only feeds the PV MFMA; summing the
     // rounded copy would cost the LSE up to 2^-9 relative on short rows).
     float psum = 0.f;
@@ -292,15 +314,19 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
       pb[kt][0] = __builtin_convertvector(p0, bf16x8);
       pb[kt][1] = __builtin_convertvector(p1, bf16x8);
+      if (dma) {
+        dma_k_part(kt, C::NKT);
+        dma_v_part(kt, C::NKT);
+      }
     }
     lrun = (rescale ? lrun * alpha : lrun) + psum;
   };
 
   // O^T += V^T P^T with the V^T tile in buffer `buf` (after the owed
   // rescale); k-step (16 keys) outer, d-tile inner, V^T fragments two k-steps
-  // ahead, and this wave's DMA of the next V^T tile (if dJ >= 0) spread
+  // ahead; with `dma`, this wave's share of the period's K DMA is spread
   // between the MFMA groups.
-  auto compute_pv = [&](int buf, int32_t dJ) {
+  auto compute_pv = [&](int buf, bool dma) __attribute__((always_inline)) {
     if (rescale) {
 #pragma unroll
       for (int tt = 0; tt < C::NDT; ++tt)
@@ -335,73 +361,81 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int tt = 0; tt < C::NDT; ++tt) fb[tt] = vfrag(tt, ks + 3);
       }
-      if (dJ >= 0) dma_slot(ks / 2, KS / 2, dJ);
+      if (dma) dma_k_part(ks / 2, KS / 2);
     }
   };
 
-  // Tile loop.  At the top of iteration t every wave waits for its own DMA of
-  // tile t and joins the barrier; the DMA of K(t+1) and V(t+1) into the ring
-  // slots freed by iteration t-1 is issued from inside the S and PV MFMA
-  // sequences of iteration t.  Head 0 of the group runs S(t) -> softmax(t) ->
-  // PV(t); head 1 runs PV(t-1) -> S(t) -> softmax(t), half a tile behind, so
-  // on each SIMD the softmax of one wave overlaps the MFMAs of the other.
-  const bool lag = HPW == 2 && hsub == 1;
-  bool pending = false;  // lagging head: P of the previous tile awaits its PV
-  int pend_vbuf = 0;
-  if (cnt > 0) {
-    uint32_t ecur = tiles[off];
+  // Tile loop: one period per tile plus one to drain.  At the top of period
+  // t every wave waits for its own DMA and joins the barrier; then K(t) and
+  // V^T(t-1) are resident, and the DMA of K(t+1) and V^T(t) goes into the
+  // ring slots that period t-1 finished reading.  Every wave runs
+  // PV(t-1) -> S(t) on the matrix core and softmax(t) on the vector ALU;
+  // head 0 of the group does so in that order, head 1 rotated by half a
+  // period: softmax(t-1) -> PV(t-1) -> S(t), holding S(t-1) across the
+  // barrier.  On each SIMD (one wave of each head) the exponentials of one
+  // wave then run while the other wave's MFMAs do, and the matrix core sees
+  // 2 x (PV + S) per period.
+  // The two orders are separate loops (chosen once per wave), so that each
+  // keeps only its own state live across the barrier: P of the previous
+  // tile for head 0, S of the previous tile for head 1.
+  auto tile_loop = [&](auto lag_c) __attribute__((always_inline)) {
+    constexpr bool LAG = decltype(lag_c)::value;
+    bool pend = false;   // the previous tile still owes this wave its PV (LAG: softmax and PV)
+    uint32_t epend = 0;  // that tile's list entry
+    uint32_t ecur = (uint32_t)__builtin_amdgcn_readfirstlane((int)tiles[off]);
+    jk = (int32_t)(ecur & TILE_J_MASK);
+    nk = 0;
 #pragma unroll
-    for (int i = 0; i < C::NI_K; ++i) dma_k(0, (int32_t)(ecur & TILE_J_MASK), i);
-#pragma unroll
-    for (int i = 0; i < C::NI_K; ++i) dma_v(0, (int32_t)(ecur & TILE_J_MASK), i);
-    for (int t = 0; t < cnt; ++t) {
-      const uint32_t enext = t + 1 < cnt ? tiles[off + t + 1] : 0u;
+    for (int i = 0; i < C::NI_K; ++i) dma_k(0, jk, i);
+    for (int t = 0; t <= cnt; ++t) {
+      const uint32_t enext =
+          t + 1 < cnt ? (uint32_t)__builtin_amdgcn_readfirstlane((int)tiles[off + t + 1]) : 0u;
       wait_vm_barrier<0>();
-      const int32_t nJ = t + 1 < cnt ? (int32_t)(enext & TILE_J_MASK) : -1;
-      nk = (t + 1) % C::KBUF;
-      nv = (t + 1) % C::VBUF;
-      const bool mine = (ecur & mybit) != 0;
-      // Each wave issues its whole DMA share of tile t+1 from the first MFMA
-      // phase it runs in this iteration, so the data has most of the tile
-      // to land before the next barrier.
-      bool issued = false;
-      if (!lag) {
+      jk = t + 1 < cnt ? (int32_t)(enext & TILE_J_MASK) : -1;
+      jv = t < cnt ? (int32_t)(ecur & TILE_J_MASK) : -1;
+      nk = (t + 1) & 1;
+      nv = t & 1;
+      const bool mine = t < cnt && (ecur & mybit) != 0;
+      bool kd = false, vd = false;  // this period's K / V^T DMA issued
+      if (!LAG) {
+        if (pend) {
+          compute_pv((t - 1) & 1, true);
+          kd = true;
+        }
         if (mine) {
-          compute_s(t % C::KBUF, nJ);
-          issued = true;
-          softmax(ecur);
-          compute_pv(t % C::VBUF, -1);
+          compute_s(t & 1, true);
+          vd = true;
+          softmax(ecur, false);
         }
       } else {
-        if (pending) {
-          compute_pv(pend_vbuf, nJ);
-          issued = true;
+        if (pend) {
+          softmax(epend, true);
+          kd = vd = true;
+          compute_pv((t - 1) & 1, false);
         }
-        if (mine) {
-          // Win the matrix core over head 0's PV for this S, so the SIMD runs
-          // h0.S, h1.PV, h1.S, h0.PV back to back with both softmaxes hidden.
-          __builtin_amdgcn_s_setprio(1);
-          compute_s(t % C::KBUF, issued ? -1 : nJ);
-          __builtin_amdgcn_s_setprio(0);
-          issued = issued || nJ >= 0;
-          softmax(ecur);
-        }
-        pending = mine;
-        pend_vbuf = t % C::VBUF;
+        if (mine) compute_s(t & 1, false);
       }
-      // A wave with no MFMA phase this iteration still issues its share.
-      if (nJ >= 0 && !issued) {
+      if (!kd) {
 #pragma unroll
-        for (int i = 0; i < C::NI_K; ++i) dma_k(nk, nJ, i);
-#pragma unroll
-        for (int i = 0; i < C::NI_K; ++i) dma_v(nv, nJ, i);
+        for (int i = 0; i < C::NI_K; ++i)
+          if (jk >= 0) dma_k(nk, jk, i);
       }
+      if (!vd) {
+#pragma unroll
+        for (int i = 0; i < C::NI_K; ++i)
+          if (jv >= 0) dma_v(nv, jv, i);
+      }
+      pend = mine;
+      epend = ecur;
       ecur = enext;
     }
-    if (pending) compute_pv(pend_vbuf, -1);
+  };
+  if (cnt > 0) {
+    if (HPW == 2 && hsub == 1) tile_loop(std::true_type());
+    else tile_loop(std::false_type());
   }
 
-  const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+  const float ltot = halves_sum(lrun);
   if (qvalid) {
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
     uint16_t* orow = o + ((tok0 + qi) * d.Hq + h) * D;

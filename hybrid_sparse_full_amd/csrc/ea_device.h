@@ -29,6 +29,25 @@ __device__ inline T wave_inclusive_sum(T v) {
   return v;
 }
 
+// A value known to be equal on every lane, stated so that it lives in SGPRs.
+__device__ inline int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uint64_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// max / sum of x over lanes l and l ^ 32 (the two half-waves), in registers:
+// v_permlane32_swap exchanges the upper half of one copy with the lower half
+// of the other, so the two results hold both halves' values on every lane.
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T>
 __device__ inline T wave_sum(T v) {
 #pragma unroll

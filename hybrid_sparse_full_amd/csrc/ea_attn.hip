@@ -200,10 +200,10 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   // DMA of one period: this wave's NI_K instructions for the K tile of
   // block jk (ring slot nk) and its NI_K for the V^T tile of block jv (ring
-  // slot nv); a block of -1 means nothing to load.  A compute phase of n
-  // steps issues, at step j, the instructions with index in
+  // slot nv); a block of -1 means nothing to load.  The softmax phase of n
+  // sub-tiles issues, at sub-tile j, the instructions with index in
   // [j * per, (j + 1) * per), per = ceil(NI_K / n), so their issue overlaps
-  // the phase's MFMAs or exponentials.
+  // the exponentials.
   int32_t jk = -1, jv = -1;
   int nk = 0, nv = 0;
   auto dma_k_part = [&](int j, int n) {
@@ -228,14 +228,19 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   // S^T = K Q^T for the B keys of the tile in K buffer `buf`.  k-step outer,
   // sub-tile inner: consecutive MFMAs use independent accumulators and the K
-  // fragments are read two k-steps ahead.  With `dma`, this wave's share of
-  // the period's V^T DMA is spread between the MFMA groups.
+  // fragments are read two k-steps ahead (the order is pinned for the
+  // scheduler).  With `dma`, this wave's share of the period's V^T DMA is
+  // issued first.
   auto compute_s = [&](int buf, bool dma) __attribute__((always_inline)) {
     const uint16_t* Ks = smem + buf * C::TILE_ELEMS;
     auto kfrag = [&](int kt, int s) {
       const int kr = 32 * kt + l32;
       return *(const bf16x8*)(Ks + kr * D + (((2 * s + half) ^ (kr & (C::KCH - 1))) * 8));
     };
+    if (dma && jv >= 0) {
+#pragma unroll
+      for (int i = 0; i < C::NI_K; ++i) dma_v(nv, jv, i);
+    }
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
@@ -261,8 +266,8 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt) fb[kt] = kfrag(kt, s + 3);
       }
-      if (dma) dma_v_part(s / 2, C::KSTEPS / 2);
     }
+    sched_reads_ahead<C::NKT, C::KSTEPS>();
   };
 
   // Token mask (flagged tiles), online-softmax statistics and P = exp2(.) in
@@ -324,9 +329,13 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   // O^T += V^T P^T with the V^T tile in buffer `buf` (after the owed
   // rescale); k-step (16 keys) outer, d-tile inner, V^T fragments two k-steps
-  // ahead; with `dma`, this wave's share of the period's K DMA is spread
-  // between the MFMA groups.
+  // ahead (order pinned); with `dma`, this wave's share of the period's K
+  // DMA is issued first.
   auto compute_pv = [&](int buf, bool dma) __attribute__((always_inline)) {
+    if (dma && jk >= 0) {
+#pragma unroll
+      for (int i = 0; i < C::NI_K; ++i) dma_k(nk, jk, i);
+    }
     if (rescale) {
 #pragma unroll
       for (int tt = 0; tt < C::NDT; ++tt)
@@ -361,8 +370,8 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int tt = 0; tt < C::NDT; ++tt) fb[tt] = vfrag(tt, ks + 3);
       }
-      if (dma) dma_k_part(ks / 2, KS / 2);
     }
+    sched_reads_ahead<C::NDT, KS>();
   };
 
   // Tile loop: one period per tile plus one to drain.  At the top of period

@@ -35,6 +35,7 @@ static ea_status make_dims(const ea_attn_desc* desc, EaDims* d) {
   d->G = a.num_q_heads / a.num_kv_heads;
   d->hpw = (d->G % 2 == 0) ? 2 : 1;
   d->ngr = d->G / d->hpw;
+  d->xa_hpi = (d->G % 4 == 0) ? 4 : (d->G % 2 == 0) ? 2 : 1;
   d->D = a.head_dim;
   d->B = a.block;
   d->S = a.xa_stride;

@@ -73,33 +73,35 @@ __global__ __launch_bounds__(META_NT) void k_seq_meta(EaDims d, const int32_t* _
     return;
   }
 
-  // 3. XA scoring pairs (sequence, q-head) in (b, h) order, with the prefix of
-  //    their triangular tile counts; zero the attended-pair counters.
-  const int64_t np = (int64_t)nseq * d.Hq;
+  // 3. XA scoring pairs (sequence, group of xa_hpi q-heads of one KV head) in
+  //    (b, group) order, with the prefix of their triangular tile counts; zero
+  //    the attended-pair counters of every (sequence, q-head).
+  for (int64_t p = tid; p < (int64_t)nseq * d.Hq; p += META_NT) xa_pairs_out[p] = 0;
+  const int nhg = d.Hq / d.xa_hpi;
+  const int64_t np = (int64_t)nseq * nhg;
   const int64_t c2 = (np + META_NT - 1) / META_NT;
   const int64_t p0 = min(np, tid * c2), p1 = min(np, p0 + c2);
   int64_t cnt = 0, items = 0;
-  for (int64_t p = p0; p < p1; ++p) {
-    const int b = (int)(p / d.Hq), h = (int)(p % d.Hq);
-    xa_pairs_out[p] = 0;
+  auto is_xa = [&](int64_t p) {
+    const int b = (int)(p / nhg), g = (int)(p % nhg) * d.xa_hpi / d.G;
     const int32_t len = m.len[b];
-    if (sane_mode(modes[(int64_t)b * d.Hkv + h / d.G]) == EA_MODE_XA && len > 0 && len % d.B == 0) {
-      const int32_t nt = cdiv(len / d.S, XA_TILE);
+    return sane_mode(modes[(int64_t)b * d.Hkv + g]) == EA_MODE_XA && len > 0 && len % d.B == 0;
+  };
+  for (int64_t p = p0; p < p1; ++p) {
+    if (is_xa(p)) {
       cnt += 1;
-      items += tri64(nt);
+      items += tri64(cdiv(m.len[p / nhg] / d.S, XA_TILE));
     }
   }
   int64_t totc, toti;
   int64_t ec = block_exclusive_sum<META_NT>(cnt, sm, &totc);
   int64_t ei = block_exclusive_sum<META_NT>(items, sm, &toti);
   for (int64_t p = p0; p < p1; ++p) {
-    const int b = (int)(p / d.Hq), h = (int)(p % d.Hq);
-    const int32_t len = m.len[b];
-    if (sane_mode(modes[(int64_t)b * d.Hkv + h / d.G]) == EA_MODE_XA && len > 0 && len % d.B == 0) {
+    if (is_xa(p)) {
       pair_bh[ec] = (int32_t)p;
       pair_items[ec] = ei;
       ec += 1;
-      ei += tri64(cdiv(len / d.S, XA_TILE));
+      ei += tri64(cdiv(m.len[p / nhg] / d.S, XA_TILE));
     }
   }
   if (tid == 0) {

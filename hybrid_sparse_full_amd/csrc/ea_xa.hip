@@ -16,7 +16,6 @@
 namespace ea {
 
 constexpr int XT = 128;  // reduced rows / columns per tile
-constexpr int XK = 64;   // k-chunk (bf16 elements) staged in LDS
 
 __device__ inline int64_t tri_root(int64_t loc) {
   int64_t t = (int64_t)((sqrt(8.0 * (double)loc + 1.0) - 1.0) * 0.5);
@@ -25,123 +24,197 @@ __device__ inline int64_t tri_root(int64_t loc) {
   return t;
 }
 
-template <int D, int R>
-__global__ __launch_bounds__(256) void k_xa_score(EaDims d, const uint16_t* __restrict__ q,
+// One scoring item is a 128 x 128 tile (reduced keys b' x reduced queries a)
+// of a group of HPI q-heads that share one KV head: the K~ chunk of every
+// stage is staged once and serves all HPI heads.  A stage is KC = 64 elements
+// of the S * d reduction (one key row t of the antidiagonal, 64 of d); rows
+// of a staged tile are 128 bytes, 16-byte chunks XOR-swizzled by row % 8.
+template <int D, int R, int HPI>
+struct XaCfg {
+  static constexpr int NW = 8;                   // waves per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int KC = 64;                  // reduction elements per stage
+  static constexpr int ROWB = KC * 2;            // bytes per staged row
+  static constexpr int OPB = XT * ROWB;          // one staged operand tile (16 KB)
+  static constexpr int STAGE = (1 + HPI) * OPB;  // K~ then HPI Q~ tiles
+  static constexpr int NS = HPI == 4 ? 2 : 3;    // stages in the LDS ring
+  static constexpr int NI = STAGE / 1024 / NW;   // 1 KB DMA regions per wave per stage
+  static constexpr int WPH = NW / HPI;           // waves per head
+  static constexpr int AW = HPI == 1 ? 4 : WPH;  // waves along a (queries)
+  static constexpr int BW = WPH / AW;            // waves along b' (keys)
+  static constexpr int NA = XT / AW / 32;        // 32-query MFMA tiles per wave
+  static constexpr int NB = XT / BW / 32;        // 32-key MFMA tiles per wave
+  static constexpr int KSTEPS = KC / 16;
+  static_assert((STAGE / 1024) % NW == 0, "DMA regions must split evenly over waves");
+};
+
+template <int D, int R, int HPI>
+__global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __restrict__ q,
                                                   const uint16_t* __restrict__ k, SeqMeta m,
-                                                  const int32_t* __restrict__ pair_bh,
+                                                  const int32_t* __restrict__ pair_bg,
                                                   const int64_t* __restrict__ pair_items,
                                                   float* __restrict__ lse_ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[XT * XK];  // K~ rows (b')
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[XT * XK];  // Q~ rows (a)
-  __shared__ int64_t item_s;
+  using C = XaCfg<D, R, HPI>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
-  const int wy = wave >> 1, wx = wave & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int hh = wv / C::WPH;                      // head of the group
+  const int wa = (wv % C::WPH) % C::AW, wb = (wv % C::WPH) / C::AW;
   const int npairs = m.scal[SCAL_XA_PAIRS];
   const int64_t total = pair_items[npairs];
   unsigned long long* ctr = (unsigned long long*)(m.scal + SCAL_CTR64);
   const float C2 = d.scale * LOG2E;
   const int S = d.S;
+  const int nhg = d.Hq / HPI;
+  const int nst = S * D / C::KC;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  // DMA: lane l of a 1 KB region writes staged row l / 8, physical chunk
+  // l % 8, which holds logical chunk (l % 8) ^ (l / 8) (row % 8 = l / 8).
+  const int rr = lane >> 3, lch = (lane & 7) ^ rr;
+  // MFMA operand reads: lane reads row 32 t + l32 at logical chunk 2 s + half.
+  const uint32_t fa = (uint32_t)l32 * C::ROWB + ((uint32_t)(l32 & 7) >> 1 << 5) +
+                      (((uint32_t)half ^ (uint32_t)(l32 & 1)) << 4);
+  volatile int64_t* item_box = (volatile int64_t*)smem;
 
   while (true) {
-    if (tid == 0) item_s = (int64_t)atomicAdd(ctr, 1ull);
+    __syncthreads();  // the previous item's readers are done with the ring
+    if (tid == 0) *item_box = (int64_t)atomicAdd(ctr, 1ull);
     __syncthreads();
-    const int64_t item = item_s;
-    __syncthreads();
+    const int64_t item = *item_box;
+    __syncthreads();  // everyone has the item before the ring is refilled
     if (item >= total) break;
     const int p = upper_index(pair_items, npairs + 1, item);
     const int64_t loc = item - pair_items[p];
     const int64_t ta = tri_root(loc);
     const int64_t tb = loc - tri64(ta);
-    const int32_t bh = pair_bh[p];
-    const int b = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
+    const int32_t bg = pair_bg[p];
+    const int b = bg / nhg, h0 = (bg % nhg) * HPI, g = h0 / d.G;
     const int64_t tok0 = m.start[b];
     const int32_t len = m.len[b];
     const int32_t nred = len / S;
     const int64_t nqb = len / d.B;
     const int32_t a0 = (int32_t)ta * XT, b0 = (int32_t)tb * XT;
 
-    f32x16 acc[2][2];
+    // Per-lane global address of each of this wave's DMA regions at t = 0,
+    // dk = 0 (rows past the sequence end read its last reduced row; their
+    // products are masked in the epilogue).
+    uint64_t gaddr[C::NI];
+    uint32_t gop[C::NI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::NI; ++i) {
+      const int jj = wv * C::NI + i;
+      const int op = jj / 16, row = 8 * (jj % 16) + rr;
+      gop[i] = (uint32_t)op;
+      if (op == 0) {
+        const int64_t bp = min(b0 + row, nred - 1);
+        const int64_t tok = tok0 + bp * S + (S - 1);
+        gaddr[i] = (uint64_t)(uintptr_t)(k + (tok * d.Hkv + g) * D + lch * 8);
+      } else {
+        const int64_t a = min(a0 + row, nred - 1);
+        const int64_t tok = tok0 + a * S;
+        gaddr[i] = (uint64_t)(uintptr_t)(q + (tok * d.Hq + h0 + op - 1) * D + lch * 8);
+      }
+    }
+    // Stage st: t = st * KC / D, dk = st * KC % D; K~ walks t backwards.
+    auto issue = [&](int st) {
+      const int t = st * C::KC / D, dk = st * C::KC % D;
+      const int64_t dK = ((int64_t)(-t) * d.Hkv * D + dk) * 2;
+      const int64_t dQ = ((int64_t)t * d.Hq * D + dk) * 2;
+      const uint32_t slot = lds0 + (uint32_t)(st % C::NS) * C::STAGE;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < C::NI; ++i) {
+        const int jj = wv * C::NI + i;
+        const uint64_t ga = gaddr[i] + (uint64_t)(gop[i] == 0 ? dK : dQ);
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(slot + (uint32_t)jj * 1024u);
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(ga), "s"(m0v)
+                     : "m0");
+      }
+    };
+
+    f32x16 acc[C::NA][C::NB];
+#pragma unroll
+    for (int i = 0; i < C::NA; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    for (int k0 = 0; k0 < S * D; k0 += XK) {
-      const int t = k0 / D, dk = k0 % D;
 #pragma unroll
-      for (int c = tid; c < XT * 8; c += 256) {
-        const int row = c >> 3, ch = c & 7;
-        const int sw = ((ch ^ (row & 7)) * 8);
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-        const int32_t bq = b0 + row, aq = a0 + row;
-        if (bq < nred)
-          kv = *(const uint4*)(k + ((tok0 + (int64_t)bq * S + (S - 1 - t)) * d.Hkv + g) * D + dk + ch * 8);
-        if (aq < nred)
-          qv = *(const uint4*)(q + ((tok0 + (int64_t)aq * S + t) * d.Hq + h) * D + dk + ch * 8);
-        *(uint4*)(As + row * XK + sw) = kv;
-        *(uint4*)(Bs + row * XK + sw) = qv;
-      }
-      __syncthreads();
+    for (int s0 = 0; s0 < C::NS - 1; ++s0)
+      if (s0 < nst) issue(s0);
+    for (int st = 0; st < nst; ++st) {
+      // Stage st has landed (own DMA) once at most the later stages' are in
+      // flight; the barrier extends that to every wave and frees the slot
+      // the next issue overwrites.
+      if (C::NS == 3 && st + 1 < nst)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(C::NI) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+      if (st + C::NS - 1 < nst) issue(st + C::NS - 1);
+      const uint32_t slot = (uint32_t)(st % C::NS) * C::STAGE;
+      const uint8_t* Ks = smem + slot + (size_t)wb * (C::NB * 32) * C::ROWB;
+      const uint8_t* Qs = smem + slot + (size_t)(1 + hh) * C::OPB + (size_t)wa * (C::NA * 32) * C::ROWB;
+      auto kf = [&](int j, int s) { return *(const bf16x8*)(Ks + (fa ^ (uint32_t)(s << 5)) + j * 32 * C::ROWB); };
+      auto qf = [&](int i, int s) { return *(const bf16x8*)(Qs + (fa ^ (uint32_t)(s << 5)) + i * 32 * C::ROWB); };
+      bf16x8 fk[2][C::NB], fq[2][C::NA];
 #pragma unroll
-      for (int ks = 0; ks < XK / 16; ++ks) {
-        const int chunk = 2 * ks + half;
-        bf16x8 af[2], bfr[2];
+      for (int j = 0; j < C::NB; ++j) fk[0][j] = kf(j, 0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = wy * 64 + 32 * i + l32;
-          af[i] = *(const bf16x8*)(As + row * XK + ((chunk ^ (row & 7)) * 8));
+      for (int i = 0; i < C::NA; ++i) fq[0][i] = qf(i, 0);
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        if (s + 1 < C::KSTEPS) {
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j) fk[(s + 1) & 1][j] = kf(j, s + 1);
+#pragma unroll
+          for (int i = 0; i < C::NA; ++i) fq[(s + 1) & 1][i] = qf(i, s + 1);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row = wx * 64 + 32 * j + l32;
-          bfr[j] = *(const bf16x8*)(Bs + row * XK + ((chunk ^ (row & 7)) * 8));
-        }
+        for (int i = 0; i < C::NA; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < C::NB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[s & 1][j], fq[s & 1][i], acc[i][j], 0, 0, 0);
       }
-      __syncthreads();
     }
 
     // Epilogue: per (reduced row a, block J) log-sum-exp in log2 units.
+    const int h = h0 + hh;
     const int64_t base_bh = (int64_t)R * (m.tri_prefix[b] * d.Hq + (int64_t)h * tri64(nqb));
-    constexpr int NG = 32 / R;      // block groups per 32-row MFMA tile
-    constexpr int RPG = R / 2;      // registers per group per lane
+    constexpr int NG = 32 / R;      // blocks per 32-key MFMA tile
+    constexpr int RPG = R / 2;      // registers per block per lane
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::NA; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int32_t a = a0 + wx * 64 + 32 * j + l32;
+      for (int j = 0; j < C::NB; ++j) {
+        const int32_t a = a0 + (wa * C::NA + i) * 32 + l32;
         const int32_t Ia = a / R;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-          const int32_t brow0 = b0 + wy * 64 + 32 * i + gi * R;
+          const int32_t brow0 = b0 + (wb * C::NB + j) * 32 + gi * R;
           const int32_t J = brow0 / R;
           float v[RPG];
           float mloc = -INFINITY;
 #pragma unroll
           for (int e = 0; e < RPG; ++e) {
             const int r = gi * RPG + e;
-            const int32_t bq = b0 + wy * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int32_t bq = b0 + (wb * C::NB + j) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             const bool ok = (bq <= a) && (a < nred);
             v[e] = ok ? acc[i][j][r] : -INFINITY;
             mloc = fmaxf(mloc, v[e]);
           }
-          const float mm = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-          float s = 0.f;
+          const float mm = halves_max(mloc);
+          float sum = 0.f;
           if (mm != -INFINITY) {
 #pragma unroll
-            for (int e = 0; e < RPG; ++e) s += exp2f((v[e] - mm) * C2);
+            for (int e = 0; e < RPG; ++e) sum += exp2f((v[e] - mm) * C2);
           }
-          s += __shfl_xor(s, 32, 64);
+          sum = halves_sum(sum);
           if (half == 0 && a < nred && J <= Ia) {
             const int64_t idx = base_bh + (int64_t)R * tri64(Ia) + (int64_t)(a - R * Ia) * (Ia + 1) + J;
-            lse_ws[idx] = mm * C2 + log2f(s);
+            lse_ws[idx] = mm * C2 + log2f(sum);
           }
         }
       }
@@ -318,21 +391,29 @@ static int device_cus() {
 hipError_t launch_xa_score(const EaDims& d, const uint16_t* q, const uint16_t* k, const SeqMeta& m,
                            void* ws, const WsLayout& L, hipStream_t st) {
   char* w = (char*)ws;
-  const int32_t* pair_bh = (const int32_t*)(w + L.xa_pair_bh);
+  const int32_t* pair_bg = (const int32_t*)(w + L.xa_pair_bh);
   const int64_t* pair_items = (const int64_t*)(w + L.xa_pair_items);
   float* lse = (float*)(w + L.xa_lse);
-  const dim3 grid((unsigned)(device_cus() * 2));
-#define EA_SCORE(DD, RR)                                                                      \
-  hipLaunchKernelGGL((k_xa_score<DD, RR>), grid, dim3(256), 0, st, d, q, k, m, pair_bh, pair_items, lse)
+  const dim3 grid((unsigned)device_cus());
+#define EA_SCORE(DD, RR, HH)                                                          \
+  hipLaunchKernelGGL((k_xa_score<DD, RR, HH>), grid, dim3(XaCfg<DD, RR, HH>::NT), 0, st, d, q, \
+                     k, m, pair_bg, pair_items, lse)
+#define EA_SCORE_H(DD, RR)                       \
+  do {                                           \
+    if (d.xa_hpi == 4) EA_SCORE(DD, RR, 4);      \
+    else if (d.xa_hpi == 2) EA_SCORE(DD, RR, 2); \
+    else EA_SCORE(DD, RR, 1);                    \
+  } while (0)
   if (d.D == 128) {
-    if (d.r == 8) EA_SCORE(128, 8);
-    else if (d.r == 16) EA_SCORE(128, 16);
-    else EA_SCORE(128, 32);
+    if (d.r == 8) EA_SCORE_H(128, 8);
+    else if (d.r == 16) EA_SCORE_H(128, 16);
+    else EA_SCORE_H(128, 32);
   } else {
-    if (d.r == 8) EA_SCORE(64, 8);
-    else if (d.r == 16) EA_SCORE(64, 16);
-    else EA_SCORE(64, 32);
+    if (d.r == 8) EA_SCORE_H(64, 8);
+    else if (d.r == 16) EA_SCORE_H(64, 16);
+    else EA_SCORE_H(64, 32);
   }
+#undef EA_SCORE_H
 #undef EA_SCORE
   return hipGetLastError();
 }

@@ -222,40 +222,27 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
 }
 
 // ---------------------------------------------------------------- selector
-constexpr int SEL_NT = 256;
-
-template <typename T>
-__device__ inline T block_max_u(T v, T* smem) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) smem[w] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    T x = smem[0];
-    for (int i = 1; i < SEL_NT / 64; ++i) x = smem[i] > x ? smem[i] : x;
-    smem[SEL_NT / 64] = x;
-  }
-  __syncthreads();
-  T res = smem[SEL_NT / 64];
-  __syncthreads();
-  return res;
-}
+// One wave per mask row (rows are independent, so no workgroup barrier is
+// needed); each wave keeps the row's block masses, weights and bits in its
+// own LDS region.
 
 template <int R>
-__global__ __launch_bounds__(SEL_NT) void k_xa_select(EaDims d, const uint8_t* __restrict__ modes,
-                                                      SeqMeta m, const float* __restrict__ lse_ws,
-                                                      uint32_t* __restrict__ mask,
-                                                      int32_t* __restrict__ row_count,
-                                                      int64_t* __restrict__ xa_pairs,
-                                                      float* __restrict__ block_mass) {
+__global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __restrict__ modes,
+                                                   SeqMeta m, const float* __restrict__ lse_ws,
+                                                   uint32_t* __restrict__ mask,
+                                                   int32_t* __restrict__ row_count,
+                                                   int64_t* __restrict__ xa_pairs,
+                                                   float* __restrict__ block_mass) {
   extern __shared__ uint32_t dyn[];
-  __shared__ float Mrow[R], Zrow[R];
-  __shared__ uint64_t red[SEL_NT / 64 + 1];
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int rpw = blockDim.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * rpw + wv;
+  if (row >= d.nqb_max * d.Hq) return;
   const int32_t qbg = (int32_t)(row / d.Hq);
   const int h = (int)(row % d.Hq);
   if (qbg >= m.scal[SCAL_TOTAL_QB]) return;
+  uint32_t* wgt = dyn + (size_t)wv * (d.maxqb + d.words);
+  uint32_t* bits = wgt + d.maxqb;
   const int32_t b = m.qb2seq[qbg];
   const int32_t I = qbg - m.qb_prefix[b];
   const int32_t len = m.len[b];
@@ -263,18 +250,18 @@ __global__ __launch_bounds__(SEL_NT) void k_xa_select(EaDims d, const uint8_t* _
   uint32_t* mrow = mask + row * d.words;
   const int32_t nI = I + 1;
   if (mode != EA_MODE_XA) {
-    for (int w = tid; w < d.words; w += SEL_NT) mrow[w] = 0u;
-    if (tid == 0) row_count[row] = 0;
+    for (int w = lane; w < d.words; w += 64) mrow[w] = 0u;
+    if (lane == 0) row_count[row] = 0;
     return;
   }
   const int64_t B = d.B;
   if (len % d.B != 0) {
     // XA on a sequence that is not a whole number of blocks: every causal block.
-    for (int w = tid; w < d.words; w += SEL_NT) {
+    for (int w = lane; w < d.words; w += 64) {
       const int hi = I - w * 32;
       mrow[w] = hi < 0 ? 0u : (hi >= 31 ? 0xffffffffu : ((2u << hi) - 1u));
     }
-    if (tid == 0) {
+    if (lane == 0) {
       row_count[row] = nI;
       const int64_t iend = min<int64_t>((int64_t)nI * B, len);
       atomicAdd((unsigned long long*)&xa_pairs[(int64_t)b * d.Hq + h],
@@ -286,97 +273,104 @@ __global__ __launch_bounds__(SEL_NT) void k_xa_select(EaDims d, const uint8_t* _
   const int64_t nqb = len / d.B;
   const float* base =
       lse_ws + (int64_t)R * (m.tri_prefix[b] * d.Hq + (int64_t)h * tri64(nqb)) + (int64_t)R * tri64(I);
-  // 1. Per reduced row a: M_a = max_J lse2, Z_a = sum_J exp2(lse2 - M_a).
+  // 1. Per reduced row a: La = log2 sum_J exp2(lse2[a, J]), one online pass
+  //    (lane-local running max and sum, then merged over the wave).
+  float La[R];
   {
-    constexpr int TPR = SEL_NT / R;
-    const int ar = tid / TPR, tj = tid % TPR;
-    const float* rw = base + (int64_t)ar * nI;
-    float mx = -INFINITY;
-    for (int J = tj; J < nI; J += TPR) mx = fmaxf(mx, rw[J]);
+    float mr[R], zr[R];
 #pragma unroll
-    for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float z = 0.f;
-    for (int J = tj; J < nI; J += TPR) z += exp2f(rw[J] - mx);
+    for (int a = 0; a < R; ++a) {
+      mr[a] = -INFINITY;
+      zr[a] = 0.f;
+    }
+#pragma unroll 2
+    for (int J = lane; J < nI; J += 64) {
 #pragma unroll
-    for (int o = TPR / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
-    if (tj == 0) {
-      Mrow[ar] = mx;
-      Zrow[ar] = z;
+      for (int a = 0; a < R; ++a) {
+        const float x = base[(int64_t)a * nI + J];
+        if (x > mr[a]) {
+          zr[a] = zr[a] * exp2f(mr[a] - x) + 1.f;
+          mr[a] = x;
+        } else {
+          zr[a] += exp2f(x - mr[a]);
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
+      const float mx = wave_max(mr[a]);
+      const float z = wave_sum(mr[a] == -INFINITY ? 0.f : zr[a] * exp2f(mr[a] - mx));
+      La[a] = mx + log2f(z);
     }
   }
-  __syncthreads();
-  // 2. Block masses and integer weights.
-  float* Pf = (float*)dyn;
-  uint32_t* wv = dyn + d.maxqb;
-  uint32_t* bits = dyn + 2 * d.maxqb;
+  // 2. Block masses P_J = (1/R) sum_a exp2(lse2[a, J] - La) and integer
+  //    weights w = max(1, floor(P * 2^24 + 1/2)).
   uint64_t wsum = 0;
   uint32_t wmax = 0;
-  for (int J = tid; J < nI; J += SEL_NT) {
+  float* bm = block_mass ? block_mass + row * d.maxqb : nullptr;
+#pragma unroll 2
+  for (int J = lane; J < nI; J += 64) {
     float acc = 0.f;
 #pragma unroll
-    for (int ar = 0; ar < R; ++ar) acc += exp2f(base[(int64_t)ar * nI + J] - Mrow[ar]) / Zrow[ar];
+    for (int a = 0; a < R; ++a) acc += exp2f(base[(int64_t)a * nI + J] - La[a]);
     const float P = acc * (1.0f / R);
-    Pf[J] = P;
+    if (bm) bm[J] = P;
     const float x = P * 16777216.0f;
     const float fl = floorf(x);
     uint32_t w = (uint32_t)fl + ((x - fl) >= 0.5f ? 1u : 0u);
     w = w < 1u ? 1u : w;
-    wv[J] = w;
+    wgt[J] = w;
     wsum += w;
     wmax = w > wmax ? w : wmax;
   }
-  for (int w = tid; w < d.words; w += SEL_NT) bits[w] = 0u;
-  const uint64_t W = block_sum<SEL_NT, uint64_t>(wsum, red);
-  const uint32_t Wmax = (uint32_t)block_max_u<uint64_t>((uint64_t)wmax, red);
+  for (int w = lane; w < d.words; w += 64) bits[w] = 0u;
+  const uint64_t W = wave_sum(wsum);
+  const uint32_t Wmax = wave_max(wmax);
   const uint64_t tn = (uint64_t)d.tau_num, td = (uint64_t)d.tau_den;
   const uint64_t target = tn * W;
   // 3. v* = largest v with (sum of w_J >= v) * td >= tn * W.
   uint32_t lo = 1, hi = Wmax + 1;
   while (hi - lo > 1) {
     const uint32_t mid = lo + (hi - lo) / 2;
-    uint64_t s = 0;
-    for (int J = tid; J < nI; J += SEL_NT) s += wv[J] >= mid ? wv[J] : 0u;
-    const uint64_t F = block_sum<SEL_NT, uint64_t>(s, red);
-    if (F * td >= target) lo = mid;
+    uint64_t sl = 0;
+    for (int J = lane; J < nI; J += 64) sl += wgt[J] >= mid ? wgt[J] : 0u;
+    if (wave_sum(sl) * td >= target) lo = mid;
     else hi = mid;
   }
   const uint32_t vstar = lo;
   uint64_t sg = 0;
-  for (int J = tid; J < nI; J += SEL_NT) sg += wv[J] > vstar ? wv[J] : 0u;
-  const uint64_t Fgt = block_sum<SEL_NT, uint64_t>(sg, red);
-  const uint64_t need = target - Fgt * td;  // > 0 by maximality of v*
+  for (int J = lane; J < nI; J += 64) sg += wgt[J] > vstar ? wgt[J] : 0u;
+  const uint64_t need = target - wave_sum(sg) * td;  // > 0 by maximality of v*
   const uint64_t vt = (uint64_t)vstar * td;
   const uint64_t ceq = (need + vt - 1) / vt;  // blocks of weight v* to take, lowest J first
   // 4. Rank of each weight-v* block among equals (J order), then set bits.
-  const int chunk = (nI + SEL_NT - 1) / SEL_NT;
-  const int j0 = min(nI, tid * chunk), j1 = min(nI, j0 + chunk);
+  const int chunk = (nI + 63) / 64;
+  const int j0 = min(nI, lane * chunk), j1 = min(nI, j0 + chunk);
   uint64_t neq = 0;
-  for (int J = j0; J < j1; ++J) neq += wv[J] == vstar;
-  uint64_t tot_eq;
-  uint64_t rank = block_exclusive_sum<SEL_NT, uint64_t>(neq, red, &tot_eq);
+  for (int J = j0; J < j1; ++J) neq += wgt[J] == vstar;
+  uint64_t rank = wave_inclusive_sum(neq) - neq;
   for (int J = j0; J < j1; ++J) {
-    bool sel = wv[J] > vstar || J == 0 || J == I;
-    if (wv[J] == vstar) {
+    bool sel = wgt[J] > vstar || J == 0 || J == I;
+    if (wgt[J] == vstar) {
       sel = sel || rank < ceq;
       ++rank;
     }
     if (sel) atomicOr(&bits[J >> 5], 1u << (J & 31));
   }
-  __syncthreads();
   uint64_t cnt = 0;
-  for (int w = tid; w < d.words; w += SEL_NT) {
-    mrow[w] = bits[w];
-    cnt += __popc(bits[w]);
+  for (int w = lane; w < d.words; w += 64) {
+    const uint32_t x = bits[w];
+    mrow[w] = x;
+    cnt += __popc(x);
   }
-  const uint64_t count = block_sum<SEL_NT, uint64_t>(cnt, red);
-  if (tid == 0) {
+  const uint64_t count = wave_sum(cnt);
+  if (lane == 0) {
     row_count[row] = (int32_t)count;
     const uint64_t pairs = (count - 1) * (uint64_t)(B * B) + (uint64_t)(B * (B + 1) / 2);
     atomicAdd((unsigned long long*)&xa_pairs[(int64_t)b * d.Hq + h], (unsigned long long)pairs);
   }
-  if (block_mass) {
-    float* bm = block_mass + row * d.maxqb;
-    for (int J = tid; J < d.maxqb; J += SEL_NT) bm[J] = J < nI ? Pf[J] : 0.f;
+  if (bm) {
+    for (int J = nI + lane; J < d.maxqb; J += 64) bm[J] = 0.f;
   }
 }
 
@@ -422,16 +416,19 @@ hipError_t launch_xa_select(const EaDims& d, const uint8_t* modes, const SeqMeta
                             const WsLayout& L, uint32_t* mask, int32_t* row_count, int64_t* xa_pairs,
                             float* block_mass, hipStream_t st) {
   const float* lse = (const float*)((char*)ws + L.xa_lse);
-  const size_t shm = (size_t)(2 * d.maxqb + d.words) * 4;
-  const dim3 grid((unsigned)(d.nqb_max * d.Hq));
+  const size_t per_row = (size_t)(d.maxqb + d.words) * 4;  // LDS per wave (row)
+  const int rpw = per_row * 4 <= 40960 ? 4 : per_row * 2 <= 40960 ? 2 : 1;
+  const int64_t rows = d.nqb_max * d.Hq;
+  const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
+  const size_t shm = per_row * rpw;
   if (d.r == 8)
-    hipLaunchKernelGGL((k_xa_select<8>), grid, dim3(SEL_NT), shm, st, d, modes, m, lse, mask,
+    hipLaunchKernelGGL((k_xa_select<8>), grid, dim3(64 * rpw), shm, st, d, modes, m, lse, mask,
                        row_count, xa_pairs, block_mass);
   else if (d.r == 16)
-    hipLaunchKernelGGL((k_xa_select<16>), grid, dim3(SEL_NT), shm, st, d, modes, m, lse, mask,
+    hipLaunchKernelGGL((k_xa_select<16>), grid, dim3(64 * rpw), shm, st, d, modes, m, lse, mask,
                        row_count, xa_pairs, block_mass);
   else
-    hipLaunchKernelGGL((k_xa_select<32>), grid, dim3(SEL_NT), shm, st, d, modes, m, lse, mask,
+    hipLaunchKernelGGL((k_xa_select<32>), grid, dim3(64 * rpw), shm, st, d, modes, m, lse, mask,
                        row_count, xa_pairs, block_mass);
   return hipGetLastError();
 }

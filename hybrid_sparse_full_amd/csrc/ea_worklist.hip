@@ -116,13 +116,14 @@ __global__ __launch_bounds__(256) void k_cost(EaDims d, const uint8_t* __restric
                                               int32_t* __restrict__ row_cost,
                                               int32_t* __restrict__ hist) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= m.scal[SCAL_N_UNITS]) return;
-  const int32_t qbg = (int32_t)(u / d.Hkv);
+  const bool valid = u < m.scal[SCAL_N_UNITS];
+  const int32_t qbg = valid ? (int32_t)(u / d.Hkv) : 0;
   const int g = (int)(u % d.Hkv);
-  const RowInfo ri = decode_qb(d, m, qbg, g, modes, xa_mask);
+  RowInfo ri = {0, 0, 0, EA_MODE_FA};
+  if (valid) ri = decode_qb(d, m, qbg, g, modes, xa_mask);
   int32_t uc = 0;
   int64_t head_tiles = 0;
-  for (int kg = 0; kg < d.ngr; ++kg) {
+  for (int kg = 0; valid && kg < d.ngr; ++kg) {
     int32_t c;
     if (ri.mode == EA_MODE_SSA) {
       int32_t jlo, ns;
@@ -151,13 +152,25 @@ __global__ __launch_bounds__(256) void k_cost(EaDims d, const uint8_t* __restric
     row_cost[u * d.ngr + kg] = c;
     uc = max(uc, c);
   }
-  atomicAdd((unsigned long long*)(m.scal + SCAL_HEAD_TILES64), (unsigned long long)head_tiles);
+  // One counter update per wave, and one histogram update per distinct cost
+  // in the wave (units of equal cost are common: every SSA row of a head).
+  const uint64_t ht = wave_sum((uint64_t)head_tiles);
+  if ((threadIdx.x & 63) == 0 && ht) atomicAdd((unsigned long long*)(m.scal + SCAL_HEAD_TILES64), ht);
+  if (!valid) return;
   unit_cost[u] = uc;
-  atomicAdd(&hist[uc], 1);
+  uint64_t todo = __ballot(1);
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int32_t c = __shfl(uc, leader, 64);
+    const uint64_t same = __ballot(uc == c) & todo;
+    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[c], (int)__popcll(same));
+    todo &= ~same;
+  }
 }
 
 // ---------------------------------------------------------------- k_sched
 constexpr int SCHED_NT = 1024;
+constexpr int SCHED_LDS_MAX = 65536;  // bytes of bucket cursors kept in LDS
 
 __global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
                                                     const int32_t* __restrict__ unit_cost,
@@ -167,6 +180,9 @@ __global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
                                                     int32_t* __restrict__ sorted_units,
                                                     int64_t* __restrict__ row_off) {
   __shared__ int64_t sm[SCHED_NT / 64 + 1];
+  extern __shared__ int32_t lcur[];  // bucket cursors (maxqb + 1), when they fit in LDS
+  const bool in_lds = (d.maxqb + 1) * 4 <= SCHED_LDS_MAX;
+  int32_t* cur = in_lds ? lcur : cursor;
   const int tid = threadIdx.x;
   const int32_t nb = d.maxqb + 1;  // costs 0..maxqb
   // Bucket starts in descending cost order: cursor[c] = sum_{c' > c} hist[c'].
@@ -178,14 +194,14 @@ __global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
     int64_t tot;
     int64_t e = block_exclusive_sum<SCHED_NT>(s, sm, &tot);
     for (int i = i0; i < i1; ++i) {
-      cursor[d.maxqb - i] = (int32_t)e;
+      cur[d.maxqb - i] = (int32_t)e;
       e += hist[d.maxqb - i];
     }
   }
   __syncthreads();
   const int32_t nu = m.scal[SCAL_N_UNITS];
   for (int32_t u = tid; u < nu; u += SCHED_NT) {
-    const int32_t pos = atomicAdd(&cursor[unit_cost[u]], 1);
+    const int32_t pos = atomicAdd(&cur[unit_cost[u]], 1);
     sorted_units[pos] = u;
   }
   // Row offsets into the flat tile list (natural row order).
@@ -287,7 +303,8 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v
   const int64_t units = d.nqb_max * d.Hkv;
   hipLaunchKernelGGL(k_cost, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, d, modes,
                      xa_mask, m, unit_cost, row_cost, hist);
-  hipLaunchKernelGGL(k_sched, dim3(1), dim3(SCHED_NT), 0, st, d, m, unit_cost, row_cost, hist,
+  const size_t sched_lds = (size_t)(d.maxqb + 1) * 4 <= (size_t)SCHED_LDS_MAX ? (size_t)(d.maxqb + 1) * 4 : 0;
+  hipLaunchKernelGGL(k_sched, dim3(1), dim3(SCHED_NT), sched_lds, st, d, m, unit_cost, row_cost, hist,
                      cursor, sorted_units, row_off);
   const int64_t rows = d.nqb_max * d.Hkv * d.ngr;
   hipLaunchKernelGGL(k_fill, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, d, modes, xa_mask,

@@ -17,7 +17,10 @@
 // every SIMD the softmax of one wave overlaps the MFMAs of the other.  The
 // DMA is issued from inline assembly and its completion is tracked by hand
 // (s_waitcnt vmcnt), because the compiler's own tracking of LDS DMA waits
-// for every outstanding load.
+// for every outstanding load.  For the same reason the work-list entries
+// reach the waves through LDS too: wave 0 copies entry n into a four-slot
+// ring by DMA three periods ahead, and every wave reads it one period ahead,
+// so no global load (and no compiler-inserted vmcnt wait) sits in the loop.
 // The LDS image of each tile row is XOR-swizzled in 16-byte chunks so that
 // the MFMA operand reads are free of bank conflicts.
 //
@@ -105,6 +108,19 @@ __device__ inline void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// 4 bytes from global memory (scalar address) into LDS at m0, issued by the
+// active lanes (one, at the call site).
+__device__ inline void dma4(const void* sbase, uint32_t lds_addr) {
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(0u), "s"((const void*)(uintptr_t)bs), "s"(lds_addr)
+               : "m0");
+}
+
 template <int D, int B, int HPW>
 __global__ __launch_bounds__(HPW * (B / 32) * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
@@ -114,6 +130,9 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
             uint16_t* __restrict__ o, float* __restrict__ lse) {
   using C = AttnCfg<D, B, HPW>;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[(C::KBUF + C::VBUF) * C::TILE_ELEMS];
+  // Ring of four list entries: entry n is copied into slot n & 3 by wave 0
+  // three periods ahead of its use and read by every wave one period ahead.
+  __shared__ uint32_t elist[4];
 
   // XCD-aware decode: blocks b, b+8, b+16, ... run on the same XCD; the head
   // groups of one unit (q-block, KV head) get consecutive slots there.
@@ -211,7 +230,7 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
     for (int x = 0; x < per; ++x) {
       const int idx = j * per + x;
-      if (idx < C::NI_K && jk >= 0) dma_k(nk, jk, idx);
+      if (idx < C::NI_K && __builtin_expect(jk >= 0, 1)) dma_k(nk, jk, idx);
     }
   };
   auto dma_v_part = [&](int j, int n) {
@@ -219,7 +238,7 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
     for (int x = 0; x < per; ++x) {
       const int idx = j * per + x;
-      if (idx < C::NI_K && jv >= 0) dma_v(nv, jv, idx);
+      if (idx < C::NI_K && __builtin_expect(jv >= 0, 1)) dma_v(nv, jv, idx);
     }
   };
 
@@ -230,17 +249,14 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   // sub-tile inner: consecutive MFMAs use independent accumulators and the K
   // fragments are read two k-steps ahead (the order is pinned for the
   // scheduler).  With `dma`, this wave's share of the period's V^T DMA is
-  // issued first.
+  // issued right after the first fragment reads, so its issue overlaps their
+  // latency.
   auto compute_s = [&](int buf, bool dma) __attribute__((always_inline)) {
     const uint16_t* Ks = smem + buf * C::TILE_ELEMS;
     auto kfrag = [&](int kt, int s) {
       const int kr = 32 * kt + l32;
       return *(const bf16x8*)(Ks + kr * D + (((2 * s + half) ^ (kr & (C::KCH - 1))) * 8));
     };
-    if (dma && jv >= 0) {
-#pragma unroll
-      for (int i = 0; i < C::NI_K; ++i) dma_v(nv, jv, i);
-    }
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
@@ -250,6 +266,10 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
     for (int kt = 0; kt < C::NKT; ++kt) fa[kt] = kfrag(kt, 0);
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) fb[kt] = kfrag(kt, 1);
+    if (dma && __builtin_expect(jv >= 0, 1)) {
+#pragma unroll
+      for (int i = 0; i < C::NI_K; ++i) dma_v(nv, jv, i);
+    }
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; s += 2) {
 #pragma unroll
@@ -330,13 +350,9 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
   // O^T += V^T P^T with the V^T tile in buffer `buf` (after the owed
   // rescale); k-step (16 keys) outer, d-tile inner, V^T fragments two k-steps
   // ahead (order pinned); with `dma`, this wave's share of the period's K
-  // DMA is issued first.
+  // DMA is issued right after the first fragment reads.
   auto compute_pv = [&](int buf, bool dma) __attribute__((always_inline)) {
-    if (dma && jk >= 0) {
-#pragma unroll
-      for (int i = 0; i < C::NI_K; ++i) dma_k(nk, jk, i);
-    }
-    if (rescale) {
+    if (__builtin_expect(rescale, 0)) {
 #pragma unroll
       for (int tt = 0; tt < C::NDT; ++tt)
 #pragma unroll
@@ -354,6 +370,10 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
     for (int tt = 0; tt < C::NDT; ++tt) fa[tt] = vfrag(tt, 0);
 #pragma unroll
     for (int tt = 0; tt < C::NDT; ++tt) fb[tt] = vfrag(tt, 1);
+    if (dma && __builtin_expect(jk >= 0, 1)) {
+#pragma unroll
+      for (int i = 0; i < C::NI_K; ++i) dma_k(nk, jk, i);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) {
 #pragma unroll
@@ -392,14 +412,21 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
     bool pend = false;   // the previous tile still owes this wave its PV (LAG: softmax and PV)
     uint32_t epend = 0;  // that tile's list entry
     uint32_t ecur = (uint32_t)__builtin_amdgcn_readfirstlane((int)tiles[off]);
+    uint32_t enext = cnt > 1 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)tiles[off + 1]) : 0u;
+    const uint32_t elds = (uint32_t)(uintptr_t)elist;
+    auto dma_entry = [&](int n) {
+      if (wv == 0 && n < cnt && lane == 0) dma4(tiles + off + n, elds + 4u * (uint32_t)(n & 3));
+    };
+    dma_entry(2);
     jk = (int32_t)(ecur & TILE_J_MASK);
     nk = 0;
 #pragma unroll
     for (int i = 0; i < C::NI_K; ++i) dma_k(0, jk, i);
     for (int t = 0; t <= cnt; ++t) {
-      const uint32_t enext =
-          t + 1 < cnt ? (uint32_t)__builtin_amdgcn_readfirstlane((int)tiles[off + t + 1]) : 0u;
       wait_vm_barrier<0>();
+      // Entry t + 2 landed with the DMA waited for above; entry t + 3 goes out now.
+      const uint32_t eraw = elist[(t + 2) & 3];
+      dma_entry(t + 3);
       jk = t + 1 < cnt ? (int32_t)(enext & TILE_J_MASK) : -1;
       jv = t < cnt ? (int32_t)(ecur & TILE_J_MASK) : -1;
       nk = (t + 1) & 1;
@@ -407,29 +434,29 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
       const bool mine = t < cnt && (ecur & mybit) != 0;
       bool kd = false, vd = false;  // this period's K / V^T DMA issued
       if (!LAG) {
-        if (pend) {
+        if (__builtin_expect(pend, 1)) {
           compute_pv((t - 1) & 1, true);
           kd = true;
         }
-        if (mine) {
+        if (__builtin_expect(mine, 1)) {
           compute_s(t & 1, true);
           vd = true;
           softmax(ecur, false);
         }
       } else {
-        if (pend) {
+        if (__builtin_expect(pend, 1)) {
           softmax(epend, true);
           kd = vd = true;
           compute_pv((t - 1) & 1, false);
         }
-        if (mine) compute_s(t & 1, false);
+        if (__builtin_expect(mine, 1)) compute_s(t & 1, false);
       }
-      if (!kd) {
+      if (__builtin_expect(!kd, 0)) {
 #pragma unroll
         for (int i = 0; i < C::NI_K; ++i)
           if (jk >= 0) dma_k(nk, jk, i);
       }
-      if (!vd) {
+      if (__builtin_expect(!vd, 0)) {
 #pragma unroll
         for (int i = 0; i < C::NI_K; ++i)
           if (jv >= 0) dma_v(nv, jv, i);
@@ -437,6 +464,7 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
       pend = mine;
       epend = ecur;
       ecur = enext;
+      enext = t + 2 < cnt ? (uint32_t)__builtin_amdgcn_readfirstlane((int)eraw) : 0u;
     }
   };
   if (cnt > 0) {

@@ -209,12 +209,12 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
           float sum = 0.f;
           if (mm != -INFINITY) {
 #pragma unroll
-            for (int e = 0; e < RPG; ++e) sum += exp2f((v[e] - mm) * C2);
+            for (int e = 0; e < RPG; ++e) sum += __builtin_amdgcn_exp2f((v[e] - mm) * C2);
           }
           sum = halves_sum(sum);
           if (half == 0 && a < nred && J <= Ia) {
             const int64_t idx = base_bh + (int64_t)R * tri64(Ia) + (int64_t)(a - R * Ia) * (Ia + 1) + J;
-            lse_ws[idx] = mm * C2 + log2f(sum);
+            lse_ws[idx] = mm * C2 + __builtin_amdgcn_logf(sum);
           }
         }
       }
@@ -289,18 +289,18 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
       for (int a = 0; a < R; ++a) {
         const float x = base[(int64_t)a * nI + J];
         if (x > mr[a]) {
-          zr[a] = zr[a] * exp2f(mr[a] - x) + 1.f;
+          zr[a] = zr[a] * __builtin_amdgcn_exp2f(mr[a] - x) + 1.f;
           mr[a] = x;
         } else {
-          zr[a] += exp2f(x - mr[a]);
+          zr[a] += __builtin_amdgcn_exp2f(x - mr[a]);
         }
       }
     }
 #pragma unroll
     for (int a = 0; a < R; ++a) {
       const float mx = wave_max(mr[a]);
-      const float z = wave_sum(mr[a] == -INFINITY ? 0.f : zr[a] * exp2f(mr[a] - mx));
-      La[a] = mx + log2f(z);
+      const float z = wave_sum(mr[a] == -INFINITY ? 0.f : zr[a] * __builtin_amdgcn_exp2f(mr[a] - mx));
+      La[a] = mx + __builtin_amdgcn_logf(z);
     }
   }
   // 2. Block masses P_J = (1/R) sum_a exp2(lse2[a, J] - La) and integer
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
   for (int J = lane; J < nI; J += 64) {
     float acc = 0.f;
 #pragma unroll
-    for (int a = 0; a < R; ++a) acc += exp2f(base[(int64_t)a * nI + J] - La[a]);
+    for (int a = 0; a < R; ++a) acc += __builtin_amdgcn_exp2f(base[(int64_t)a * nI + J] - La[a]);
     const float P = acc * (1.0f / R);
     if (bm) bm[J] = P;
     const float x = P * 16777216.0f;

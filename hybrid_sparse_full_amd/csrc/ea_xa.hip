@@ -285,15 +285,17 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
     }
 #pragma unroll 2
     for (int J = lane; J < nI; J += 64) {
+      float x[R];
+#pragma unroll
+      for (int a = 0; a < R; ++a) x[a] = base[(int64_t)a * nI + J];
+      // Branch-free update (a divergent branch here made the compiler
+      // shuffle all 2R running values on every element).
 #pragma unroll
       for (int a = 0; a < R; ++a) {
-        const float x = base[(int64_t)a * nI + J];
-        if (x > mr[a]) {
-          zr[a] = zr[a] * __builtin_amdgcn_exp2f(mr[a] - x) + 1.f;
-          mr[a] = x;
-        } else {
-          zr[a] += __builtin_amdgcn_exp2f(x - mr[a]);
-        }
+        const float mn = fmaxf(mr[a], x[a]);
+        const float mb = mn == -INFINITY ? 0.f : mn;
+        zr[a] = zr[a] * __builtin_amdgcn_exp2f(mr[a] - mb) + __builtin_amdgcn_exp2f(x[a] - mb);
+        mr[a] = mn;
       }
     }
 #pragma unroll

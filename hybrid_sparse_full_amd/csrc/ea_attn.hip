@@ -38,8 +38,8 @@
 // Softmax: exp2 with the scale c*log2(e) folded into one FMA; the reference
 // max is shared by both half-waves (v_permlane32_swap, no LDS) and moves only
 // when a row max exceeds it by more than 2^8 in the exp2 domain, so O and l
-// are rescaled rarely; P stays below 256, which bf16 and fp32 hold exactly
-// as well as values below 1.
+// are rescaled rarely; P stays at most 2^8, far inside the range of bf16 and
+// fp32, and keeps their relative precision.
 #include "ea_device.h"
 
 namespace ea {

@@ -185,39 +185,47 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
     const int64_t base_bh = (int64_t)R * (m.tri_prefix[b] * d.Hq + (int64_t)h * tri64(nqb));
     constexpr int NG = 32 / R;      // blocks per 32-key MFMA tile
     constexpr int RPG = R / 2;      // registers per block per lane
+    // A tile strictly below the diagonal block row and inside the sequence
+    // needs neither the causal nor the range test.
+    const bool interior = b0 + XT <= a0 && a0 + XT <= nred;
+    auto epilogue = [&](auto full_c) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-    for (int i = 0; i < C::NA; ++i)
+      for (int i = 0; i < C::NA; ++i)
 #pragma unroll
-      for (int j = 0; j < C::NB; ++j) {
-        const int32_t a = a0 + (wa * C::NA + i) * 32 + l32;
-        const int32_t Ia = a / R;
+        for (int j = 0; j < C::NB; ++j) {
+          const int32_t a = a0 + (wa * C::NA + i) * 32 + l32;
+          const int32_t Ia = a / R;
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const int32_t brow0 = b0 + (wb * C::NB + j) * 32 + gi * R;
-          const int32_t J = brow0 / R;
-          float v[RPG];
-          float mloc = -INFINITY;
+          for (int gi = 0; gi < NG; ++gi) {
+            const int32_t brow0 = b0 + (wb * C::NB + j) * 32 + gi * R;
+            const int32_t J = brow0 / R;
+            float v[RPG];
+            float mloc = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < RPG; ++e) {
-            const int r = gi * RPG + e;
-            const int32_t bq = b0 + (wb * C::NB + j) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = (bq <= a) && (a < nred);
-            v[e] = ok ? acc[i][j][r] : -INFINITY;
-            mloc = fmaxf(mloc, v[e]);
-          }
-          const float mm = halves_max(mloc);
-          float sum = 0.f;
-          if (mm != -INFINITY) {
+            for (int e = 0; e < RPG; ++e) {
+              const int r = gi * RPG + e;
+              const int32_t bq = b0 + (wb * C::NB + j) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              const bool ok = FULL || ((bq <= a) && (a < nred));
+              v[e] = ok ? acc[i][j][r] : -INFINITY;
+              mloc = fmaxf(mloc, v[e]);
+            }
+            const float mm = halves_max(mloc);
+            float sum = 0.f;
+            if (FULL || mm != -INFINITY) {
 #pragma unroll
-            for (int e = 0; e < RPG; ++e) sum += __builtin_amdgcn_exp2f((v[e] - mm) * C2);
-          }
-          sum = halves_sum(sum);
-          if (half == 0 && a < nred && J <= Ia) {
-            const int64_t idx = base_bh + (int64_t)R * tri64(Ia) + (int64_t)(a - R * Ia) * (Ia + 1) + J;
-            lse_ws[idx] = mm * C2 + __builtin_amdgcn_logf(sum);
+              for (int e = 0; e < RPG; ++e) sum += __builtin_amdgcn_exp2f((v[e] - mm) * C2);
+            }
+            sum = halves_sum(sum);
+            if (half == 0 && (FULL || (a < nred && J <= Ia))) {
+              const int64_t idx = base_bh + (int64_t)R * tri64(Ia) + (int64_t)(a - R * Ia) * (Ia + 1) + J;
+              lse_ws[idx] = mm * C2 + __builtin_amdgcn_logf(sum);
+            }
           }
         }
-      }
+    };
+    if (interior) epilogue(std::true_type());
+    else epilogue(std::false_type());
   }
 }
 

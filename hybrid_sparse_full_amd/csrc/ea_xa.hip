@@ -340,12 +340,31 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
   const uint64_t target = tn * W;
   // 3. v* = largest v with (sum of w_J >= v) * td >= tn * W.
   uint32_t lo = 1, hi = Wmax + 1;
-  while (hi - lo > 1) {
-    const uint32_t mid = lo + (hi - lo) / 2;
-    uint64_t sl = 0;
-    for (int J = lane; J < nI; J += 64) sl += wgt[J] >= mid ? wgt[J] : 0u;
-    if (wave_sum(sl) * td >= target) lo = mid;
-    else hi = mid;
+  constexpr int WREG = 32;  // rows of up to 64 * WREG blocks search from registers
+  if (nI <= 64 * WREG) {
+    uint32_t wr[WREG];
+#pragma unroll
+    for (int k = 0; k < WREG; ++k) {
+      const int J = lane + 64 * k;
+      const uint32_t x = wgt[J < nI ? J : 0];
+      wr[k] = J < nI ? x : 0u;
+    }
+    while (hi - lo > 1) {
+      const uint32_t mid = lo + (hi - lo) / 2;
+      uint32_t sl = 0;  // WREG weights of at most 2^24 + 1 each
+#pragma unroll
+      for (int k = 0; k < WREG; ++k) sl += wr[k] >= mid ? wr[k] : 0u;
+      if (wave_sum((uint64_t)sl) * td >= target) lo = mid;
+      else hi = mid;
+    }
+  } else {
+    while (hi - lo > 1) {
+      const uint32_t mid = lo + (hi - lo) / 2;
+      uint64_t sl = 0;
+      for (int J = lane; J < nI; J += 64) sl += wgt[J] >= mid ? wgt[J] : 0u;
+      if (wave_sum(sl) * td >= target) lo = mid;
+      else hi = mid;
+    }
   }
   const uint32_t vstar = lo;
   uint64_t sg = 0;

@@ -26,7 +26,7 @@ static ea_status make_dims(const ea_attn_desc* desc, EaDims* d) {
   if (a.block != 64 && a.block != 128) return EA_ERR_UNSUPPORTED;
   if (a.block % a.xa_stride) return EA_ERR_INVALID_ARG;
   const int r = a.block / a.xa_stride;
-  if (r != 8 && r != 16 && r != 32) return EA_ERR_UNSUPPORTED;
+  if (r != 4 && r != 8 && r != 16 && r != 32) return EA_ERR_UNSUPPORTED;
   d->nseq = a.num_seqs;
   d->T = a.total_tokens;
   d->maxL = a.max_seqlen;

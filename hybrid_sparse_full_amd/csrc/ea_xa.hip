@@ -183,8 +183,12 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
     // Epilogue: per (reduced row a, block J) log-sum-exp in log2 units.
     const int h = h0 + hh;
     const int64_t base_bh = (int64_t)R * (m.tri_prefix[b] * d.Hq + (int64_t)h * tri64(nqb));
-    constexpr int NG = 32 / R;      // blocks per 32-key MFMA tile
-    constexpr int RPG = R / 2;      // registers per block per lane
+    // Register r of a lane holds reduced key 8 (r >> 2) + 4 half + (r & 3) of
+    // the 32-key MFMA tile.  With R >= 8 a block spans both half-waves (R / 2
+    // registers per lane); with R == 4 it lies in one half-wave: registers
+    // 4k..4k+3 of half h hold block 2k + h.
+    constexpr int NG = R >= 8 ? 32 / R : 4;  // blocks per 32-key MFMA tile per lane
+    constexpr int RPG = R >= 8 ? R / 2 : 4;  // registers per block per lane
     // A tile strictly below the diagonal block row and inside the sequence
     // needs neither the causal nor the range test.
     const bool interior = b0 + XT <= a0 && a0 + XT <= nred;
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
           const int32_t Ia = a / R;
 #pragma unroll
           for (int gi = 0; gi < NG; ++gi) {
-            const int32_t brow0 = b0 + (wb * C::NB + j) * 32 + gi * R;
+            const int32_t brow0 = b0 + (wb * C::NB + j) * 32 + (R >= 8 ? gi * R : 8 * gi + 4 * half);
             const int32_t J = brow0 / R;
             float v[RPG];
             float mloc = -INFINITY;
@@ -210,14 +214,14 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
               v[e] = ok ? acc[i][j][r] : -INFINITY;
               mloc = fmaxf(mloc, v[e]);
             }
-            const float mm = halves_max(mloc);
+            const float mm = R >= 8 ? halves_max(mloc) : mloc;
             float sum = 0.f;
             if (FULL || mm != -INFINITY) {
 #pragma unroll
               for (int e = 0; e < RPG; ++e) sum += __builtin_amdgcn_exp2f((v[e] - mm) * C2);
             }
-            sum = halves_sum(sum);
-            if (half == 0 && (FULL || (a < nred && J <= Ia))) {
+            if (R >= 8) sum = halves_sum(sum);
+            if ((R < 8 || half == 0) && (FULL || (a < nred && J <= Ia))) {
               const int64_t idx = base_bh + (int64_t)R * tri64(Ia) + (int64_t)(a - R * Ia) * (Ia + 1) + J;
               lse_ws[idx] = mm * C2 + __builtin_amdgcn_logf(sum);
             }
@@ -428,11 +432,13 @@ hipError_t launch_xa_score(const EaDims& d, const uint16_t* q, const uint16_t* k
     else EA_SCORE(DD, RR, 1);                    \
   } while (0)
   if (d.D == 128) {
-    if (d.r == 8) EA_SCORE_H(128, 8);
+    if (d.r == 4) EA_SCORE_H(128, 4);
+    else if (d.r == 8) EA_SCORE_H(128, 8);
     else if (d.r == 16) EA_SCORE_H(128, 16);
     else EA_SCORE_H(128, 32);
   } else {
-    if (d.r == 8) EA_SCORE_H(64, 8);
+    if (d.r == 4) EA_SCORE_H(64, 4);
+    else if (d.r == 8) EA_SCORE_H(64, 8);
     else if (d.r == 16) EA_SCORE_H(64, 16);
     else EA_SCORE_H(64, 32);
   }
@@ -450,7 +456,10 @@ hipError_t launch_xa_select(const EaDims& d, const uint8_t* modes, const SeqMeta
   const int64_t rows = d.nqb_max * d.Hq;
   const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
   const size_t shm = per_row * rpw;
-  if (d.r == 8)
+  if (d.r == 4)
+    hipLaunchKernelGGL((k_xa_select<4>), grid, dim3(64 * rpw), shm, st, d, modes, m, lse, mask,
+                       row_count, xa_pairs, block_mass);
+  else if (d.r == 8)
     hipLaunchKernelGGL((k_xa_select<8>), grid, dim3(64 * rpw), shm, st, d, modes, m, lse, mask,
                        row_count, xa_pairs, block_mass);
   else if (d.r == 16)

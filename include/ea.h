@@ -66,7 +66,7 @@ typedef struct {
   float softmax_scale;   /* c > 0, usually 1/sqrt(d) */
   int32_t ssa_sink;      /* s >= 0: keys j < s are always kept by SSA */
   int32_t ssa_window;    /* W >= 1: SSA keeps keys with i - j < W */
-  int32_t xa_stride;     /* S: divides B with B/S in {8, 16, 32} */
+  int32_t xa_stride;     /* S: divides B with B/S in {4, 8, 16, 32} */
   int32_t xa_tau_num;    /* tau = num/den, 0 < tau <= 1, den <= 2^20 */
   int32_t xa_tau_den;
 } ea_attn_desc;

@@ -100,6 +100,14 @@ CONFIGS = {
         seqlens=(65536,), modes=_row(xa=(0, 4)), sparse_mode=MODE_SSA,
         needle_layout="clustered", needle_blocks_per_64k=16,
         description="batch 1, seq 65536, 32/8 heads, d 128, XA {0,4} (block 128, stride 8, tau 0.9) + 6 SSA (sink 128, window 4096)"),
+    # The same XA-SSA layer with the XA parameters of the pages' Table 8:
+    # block 64 and stride 16 (4 reduced rows per block); kernel tiles of 64.
+    "xassa-64k-b64s16": Config(
+        name="xassa-64k-b64s16", seed=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block=64, ssa_sink=128, ssa_window=4096, xa_stride=16,
+        seqlens=(65536,), modes=_row(xa=(0, 4)), sparse_mode=MODE_SSA,
+        needle_layout="clustered", needle_blocks_per_64k=16,
+        description="batch 1, seq 65536, 32/8 heads, d 128, XA {0,4} (block 64, stride 16, tau 0.9) + 6 SSA (sink 128, window 4096)"),
     # Qwen3-8B-shaped 256K prefill, two mode sets over the same tensors.
     "qwen8b-faxa-256k": Config(
         name="qwen8b-faxa-256k", seed=4, num_q_heads=32, num_kv_heads=8,

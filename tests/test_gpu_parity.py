@@ -67,6 +67,17 @@ def test_xa_masks_many_rows():
             assert gout["xa_pairs"][b, h] == OX.kept_pairs(M, L, cfg.block)
 
 
+@pytest.mark.parametrize("B,S", [(64, 16), (128, 32)])
+def test_xa_four_reduced_rows_per_block(B, S):
+    # B / S = 4: each block of a 32-key MFMA tile lies in one half-wave.
+    cfg = _small(name=f"xa-r4-B{B}", seqlens=(32 * B, 13 * B), num_q_heads=8, num_kv_heads=2,
+                 block=B, xa_stride=S, modes=((MODE_XA, MODE_SSA), (MODE_XA, MODE_XA)),
+                 needle_layout="clustered", needle_blocks_per_64k=512)
+    inp = make_inputs(cfg)
+    gout, masks, stats = _full_check(inp, f"xa-r4 B{B} S{S}")
+    assert stats["rows"] > 40
+
+
 def _all_fa(inp):
     inp1 = dict(inp)
     inp1["modes"] = np.zeros_like(inp["modes"])
@@ -168,6 +179,10 @@ def test_llama8b_fassa_64k_sampled():
 
 def test_xassa_64k_sampled():
     _sampled_check("xassa-64k", 192, 3)
+
+
+def test_xassa_64k_b64s16_sampled():
+    _sampled_check("xassa-64k-b64s16", 192, 6)
 
 
 def test_ragged_8x_sampled():

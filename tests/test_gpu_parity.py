@@ -67,6 +67,20 @@ def test_xa_masks_many_rows():
             assert gout["xa_pairs"][b, h] == OX.kept_pairs(M, L, cfg.block)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,B", [(4, 4, 128, 128), (4, 2, 128, 128), (6, 2, 128, 128),
+                                         (6, 2, 64, 64), (3, 3, 64, 128)])
+def test_gqa_group_sizes(Hq, Hkv, D, B):
+    # Group sizes 1, 2 and 3: one head per attention workgroup when G is odd,
+    # and 1 or 2 heads per XA scoring item.
+    modes = ((MODE_XA,) + (MODE_SSA, MODE_FA) * Hkv)[:Hkv]
+    modes2 = ((MODE_FA,) + (MODE_XA, MODE_SSA) * Hkv)[:Hkv]
+    cfg = _small(name=f"gqa-{Hq}-{Hkv}", seqlens=(12 * B, 7 * B + 5, 5 * B), num_q_heads=Hq,
+                 num_kv_heads=Hkv, head_dim=D, block=B, xa_stride=B // 16,
+                 modes=(modes, modes2, modes))
+    inp = make_inputs(cfg)
+    _full_check(inp, f"gqa Hq{Hq} Hkv{Hkv} D{D} B{B}")
+
+
 @pytest.mark.parametrize("B,S", [(64, 16), (128, 32)])
 def test_xa_four_reduced_rows_per_block(B, S):
     # B / S = 4: each block of a 32-key MFMA tile lies in one half-wave.

@@ -197,19 +197,16 @@ ea_status ea_xa_block_select(const ea_attn_desc* desc, const void* q_dev, const 
   return EA_OK;
 }
 
-ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
-                                 const void* v_dev, const int32_t* cu_seqlens_dev,
-                                 const uint8_t* modes_dev, const uint32_t* xa_mask_dev,
-                                 void* o_out_dev, float* lse_out_dev, void* workspace_dev,
-                                 size_t workspace_bytes, void* stream) {
+ea_status ea_hybrid_attn_plan(const ea_attn_desc* desc, const void* k_dev, const void* v_dev,
+                              const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                              const uint32_t* xa_mask_dev, void* workspace_dev,
+                              size_t workspace_bytes, void* stream) {
   EaDims d;
   ea_status st = make_dims(desc, &d);
   if (st != EA_OK) return st;
   if (!cu_seqlens_dev || !modes_dev) return EA_ERR_INVALID_ARG;
-  if (d.T > 0 && (!q_dev || !k_dev || !v_dev || !o_out_dev || !lse_out_dev))
-    return EA_ERR_INVALID_ARG;
-  if (misaligned(q_dev) || misaligned(k_dev) || misaligned(v_dev) || misaligned(o_out_dev))
-    return EA_ERR_INVALID_ARG;
+  if (d.T > 0 && (!k_dev || !v_dev)) return EA_ERR_INVALID_ARG;
+  if (misaligned(k_dev) || misaligned(v_dev)) return EA_ERR_INVALID_ARG;
   WsLayout L;
   const size_t need = ws_layout(d, EA_OP_PREFILL, &L);
   if (!workspace_dev || workspace_bytes < need) return EA_ERR_WORKSPACE;
@@ -219,13 +216,49 @@ ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, co
   if (launch_seq_meta(d, cu_seqlens_dev, modes_dev, m, workspace_dev, L, false, nullptr, s) !=
       hipSuccess)
     return EA_ERR_HIP;
-  if (launch_worklist(d, (const uint16_t*)k_dev, (const uint16_t*)v_dev, modes_dev, xa_mask_dev, m, workspace_dev, L, s) !=
-      hipSuccess)
-    return EA_ERR_HIP;
-  if (launch_attention(d, (const uint16_t*)q_dev, modes_dev, m,
-                       workspace_dev, L, (uint16_t*)o_out_dev, lse_out_dev, s) != hipSuccess)
+  if (launch_worklist(d, (const uint16_t*)k_dev, (const uint16_t*)v_dev, modes_dev, xa_mask_dev,
+                      m, workspace_dev, L, s) != hipSuccess)
     return EA_ERR_HIP;
   return EA_OK;
+}
+
+ea_status ea_hybrid_attn_run(const ea_attn_desc* desc, const void* q_dev,
+                             const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
+                             void* workspace_dev, size_t workspace_bytes, void* stream) {
+  EaDims d;
+  ea_status st = make_dims(desc, &d);
+  if (st != EA_OK) return st;
+  if (!modes_dev) return EA_ERR_INVALID_ARG;
+  if (d.T > 0 && (!q_dev || !o_out_dev || !lse_out_dev)) return EA_ERR_INVALID_ARG;
+  if (misaligned(q_dev) || misaligned(o_out_dev)) return EA_ERR_INVALID_ARG;
+  WsLayout L;
+  const size_t need = ws_layout(d, EA_OP_PREFILL, &L);
+  if (!workspace_dev || workspace_bytes < need) return EA_ERR_WORKSPACE;
+  if (d.T == 0) return EA_OK;
+  SeqMeta m = seq_meta_ptrs(L, workspace_dev);
+  if (launch_attention(d, (const uint16_t*)q_dev, modes_dev, m, workspace_dev, L,
+                       (uint16_t*)o_out_dev, lse_out_dev, (hipStream_t)stream) != hipSuccess)
+    return EA_ERR_HIP;
+  return EA_OK;
+}
+
+ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
+                                 const void* v_dev, const int32_t* cu_seqlens_dev,
+                                 const uint8_t* modes_dev, const uint32_t* xa_mask_dev,
+                                 void* o_out_dev, float* lse_out_dev, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream) {
+  // Validate everything before the first launch: run's checks are made here
+  // too, so a bad q / o / lse never leaves a half-done plan behind.
+  EaDims d;
+  ea_status st = make_dims(desc, &d);
+  if (st != EA_OK) return st;
+  if (d.T > 0 && (!q_dev || !o_out_dev || !lse_out_dev)) return EA_ERR_INVALID_ARG;
+  if (misaligned(q_dev) || misaligned(o_out_dev)) return EA_ERR_INVALID_ARG;
+  st = ea_hybrid_attn_plan(desc, k_dev, v_dev, cu_seqlens_dev, modes_dev, xa_mask_dev,
+                           workspace_dev, workspace_bytes, stream);
+  if (st != EA_OK) return st;
+  return ea_hybrid_attn_run(desc, q_dev, modes_dev, o_out_dev, lse_out_dev, workspace_dev,
+                            workspace_bytes, stream);
 }
 
 ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu, const uint8_t* modes,

@@ -28,7 +28,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libea.so")
 # Every symbol include/ea.h declares.
 EXPORTS = (
     "ea_workspace_bytes", "ea_mask_rows", "ea_mask_words", "ea_workspace_offset",
-    "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_sparsity_ratios", "ea_status_string",
+    "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_hybrid_attn_plan", "ea_hybrid_attn_run",
+    "ea_sparsity_ratios", "ea_status_string",
 )
 
 
@@ -79,6 +80,10 @@ def lib():
     L.ea_xa_block_select.restype = ctypes.c_int
     L.ea_hybrid_attn_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.ea_hybrid_attn_prefill.restype = ctypes.c_int
+    L.ea_hybrid_attn_plan.argtypes = [D, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.ea_hybrid_attn_plan.restype = ctypes.c_int
+    L.ea_hybrid_attn_run.argtypes = [D, P, P, P, P, P, ctypes.c_size_t, P]
+    L.ea_hybrid_attn_run.restype = ctypes.c_int
     L.ea_sparsity_ratios.argtypes = [D, P, P, ctypes.c_uint8, P, P, P, P, P]
     L.ea_sparsity_ratios.restype = ctypes.c_int
     L.ea_status_string.argtypes = [ctypes.c_int]
@@ -151,6 +156,22 @@ def ea_hybrid_attn_prefill(desc, q, k, v, cu_seqlens, modes, xa_mask, o_out, lse
         _nbytes(workspace) if workspace is not None else 0, _stream(stream))
     if st != EA_OK:
         raise EaError(st, "ea_hybrid_attn_prefill")
+
+
+def ea_hybrid_attn_plan(desc, k, v, cu_seqlens, modes, xa_mask, workspace, stream=None):
+    st = lib().ea_hybrid_attn_plan(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(modes), _ptr(xa_mask),
+        _ptr(workspace), _nbytes(workspace) if workspace is not None else 0, _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_hybrid_attn_plan")
+
+
+def ea_hybrid_attn_run(desc, q, modes, o_out, lse_out, workspace, stream=None):
+    st = lib().ea_hybrid_attn_run(
+        ctypes.byref(desc), _ptr(q), _ptr(modes), _ptr(o_out), _ptr(lse_out), _ptr(workspace),
+        _nbytes(workspace) if workspace is not None else 0, _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_hybrid_attn_run")
 
 
 def ea_sparsity_ratios(desc, cu_seqlens_host, modes_host, sparse_mode, xa_pairs_host,

@@ -68,6 +68,13 @@ class HybridPrefill:
                                  self.mask if self.has_xa else None, self.o, self.lse,
                                  self.ws_prefill, stream)
 
+    def plan(self, k, v, stream=None):
+        E.ea_hybrid_attn_plan(self.desc, k, v, self.cu, self.modes,
+                              self.mask if self.has_xa else None, self.ws_prefill, stream)
+
+    def run(self, q, stream=None):
+        E.ea_hybrid_attn_run(self.desc, q, self.modes, self.o, self.lse, self.ws_prefill, stream)
+
     def __call__(self, q, k, v, stream=None):
         if self.has_xa:
             self.select(q, k, stream)

@@ -156,6 +156,32 @@ ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, co
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * The same prefill in two calls, for callers that schedule or time the
+ * attention launch on its own.  ea_hybrid_attn_prefill is exactly
+ * ea_hybrid_attn_plan followed by ea_hybrid_attn_run.
+ *
+ * ea_hybrid_attn_plan: validates the arguments, then writes into the
+ *   workspace the per-sequence metadata, the work list (cost-sorted rows and
+ *   their flagged kv tiles) and the packed K / V^T tiles.  Arguments mean
+ *   what they mean for ea_hybrid_attn_prefill; q, o and lse are not used.
+ * ea_hybrid_attn_run: launches the attention kernel over that plan.  It must
+ *   follow a successful plan call on the same stream with the same
+ *   descriptor, modes_dev and workspace, and k, v, cu_seqlens and the mask
+ *   unchanged since; the library cannot check that pairing and reads
+ *   whatever the workspace holds.  Writes o_out_dev and lse_out_dev as
+ *   ea_hybrid_attn_prefill does.
+ * Both return EA_ERR_* on invalid arguments before any launch, and
+ * EA_ERR_HIP if a launch fails.
+ */
+ea_status ea_hybrid_attn_plan(const ea_attn_desc* desc, const void* k_dev, const void* v_dev,
+                              const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                              const uint32_t* xa_mask_dev, void* workspace_dev,
+                              size_t workspace_bytes, void* stream);
+ea_status ea_hybrid_attn_run(const ea_attn_desc* desc, const void* q_dev,
+                             const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
+                             void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
  * Model and effective sparsity ratios (Eq. 4 and Eq. 5 of the Chinese
  * paper-reading notes, section on the two sparsity ratios), computed on the
  * host, synchronously.  One layer; the average runs over the KV heads of a

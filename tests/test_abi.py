@@ -113,6 +113,41 @@ def test_prefill_rejects_null_and_misaligned_and_small_workspace():
                                       None, FAKE, need0, None) == E.EA_OK
 
 
+def test_plan_and_run_reject_null_misaligned_and_small_workspace():
+    lib = E.lib()
+    d = desc()
+    need = E.ea_workspace_bytes(d, E.EA_OP_PREFILL)
+    plan = [FAKE, FAKE, FAKE, FAKE, None, FAKE, need, None]   # k v cu modes mask ws bytes stream
+    run = [FAKE, FAKE, FAKE, FAKE, FAKE, need, None]          # q modes o lse ws bytes stream
+    assert lib.ea_hybrid_attn_plan(None, *plan) == E.EA_ERR_INVALID_ARG
+    assert lib.ea_hybrid_attn_run(None, *run) == E.EA_ERR_INVALID_ARG
+    for i in (0, 1, 2, 3):                   # k v cu modes
+        a = list(plan)
+        a[i] = None
+        assert lib.ea_hybrid_attn_plan(ctypes.byref(d), *a) == E.EA_ERR_INVALID_ARG, i
+    for i in (0, 1, 2, 3):                   # q modes o lse
+        a = list(run)
+        a[i] = None
+        assert lib.ea_hybrid_attn_run(ctypes.byref(d), *a) == E.EA_ERR_INVALID_ARG, i
+    for i in (0, 1):                         # k v need 16-byte alignment
+        a = list(plan)
+        a[i] = FAKE + 2
+        assert lib.ea_hybrid_attn_plan(ctypes.byref(d), *a) == E.EA_ERR_INVALID_ARG, i
+    for i in (0, 2):                         # q o
+        a = list(run)
+        a[i] = FAKE + 2
+        assert lib.ea_hybrid_attn_run(ctypes.byref(d), *a) == E.EA_ERR_INVALID_ARG, i
+    a = list(plan)
+    a[6] = need - 1
+    assert lib.ea_hybrid_attn_plan(ctypes.byref(d), *a) == E.EA_ERR_WORKSPACE
+    a = list(run)
+    a[4] = None
+    assert lib.ea_hybrid_attn_run(ctypes.byref(d), *a) == E.EA_ERR_WORKSPACE
+    # A bad q, o or lse makes the one-call prefill fail before its plan runs.
+    args = [None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None]
+    assert lib.ea_hybrid_attn_prefill(ctypes.byref(d), *args) == E.EA_ERR_INVALID_ARG
+
+
 def test_select_rejects_small_workspace_and_nulls():
     lib = E.lib()
     d = desc()

@@ -137,6 +137,25 @@ def test_eq3_concatenation_bitwise():
                     assert np.array_equal(hyb["lse"][h, sl], one["lse"][h, sl])
 
 
+def test_plan_then_run_equals_prefill():
+    # ea_hybrid_attn_plan + ea_hybrid_attn_run is the one-call prefill, and a
+    # second run over the same plan gives the same result.
+    import torch
+    cfg = _small(seqlens=(768, 300), modes=((MODE_XA, MODE_SSA), (MODE_FA, MODE_XA)))
+    inp = make_inputs(cfg)
+    ref = PU.run_gpu(inp)
+    layer = ref["layer"]
+    layer.o.zero_()
+    layer.lse.zero_()
+    layer.plan(ref["k"], ref["v"])
+    for _ in range(2):
+        layer.run(ref["q"])
+        torch.cuda.synchronize()
+        o = layer.o.float().cpu().numpy().astype(np.float64)
+        lse = layer.lse.cpu().numpy().astype(np.float64)
+        assert np.array_equal(o, ref["o"]) and np.array_equal(lse, ref["lse"])
+
+
 def test_deterministic():
     cfg = _small(seqlens=(640, 300), modes=((MODE_XA, MODE_SSA), (MODE_FA, MODE_XA)))
     inp = make_inputs(cfg)

@@ -137,6 +137,45 @@ def test_eq3_concatenation_bitwise():
                     assert np.array_equal(hyb["lse"][h, sl], one["lse"][h, sl])
 
 
+def test_xa_tile_list_is_the_union():
+    # Each XA row lists the union of its two heads' mask rows once, in J
+    # order, each entry flagged with the heads that attend it.
+    from hybrid_sparse_full_amd import ea as E
+    cfg = _small(name="xa-order", seqlens=(3072, 1280), modes=((MODE_XA, MODE_SSA), (MODE_XA, MODE_XA)),
+                 needle_layout="clustered", needle_blocks_per_64k=512)
+    inp = make_inputs(cfg)
+    gout = PU.run_gpu(inp)
+    layer = gout["layer"]
+    ws = layer.ws_prefill.cpu().numpy()
+    off = lambda name: E.ea_workspace_offset(layer.desc, E.EA_OP_PREFILL, name)
+    def arr(name, dt):
+        a = ws[off(name):]
+        n = len(a) // np.dtype(dt).itemsize
+        return a[: n * np.dtype(dt).itemsize].view(dt)
+    tiles, row_off, row_cost = arr("tiles", np.uint32), arr("row_off", np.int64), arr("row_cost", np.int32)
+    G, hpw, Hkv = cfg.gqa, 2, cfg.num_kv_heads
+    P = PU.qb_prefix(inp["seqlens"], cfg.block)
+    checked = 0
+    for b in range(len(inp["seqlens"])):
+        for I in range(int(P[b + 1] - P[b])):
+            qbg = int(P[b]) + I
+            for g in range(Hkv):
+                if inp["modes"][b, g] != MODE_XA:
+                    continue
+                for kg in range(G // hpw):
+                    row = (qbg * Hkv + g) * (G // hpw) + kg
+                    ent = tiles[row_off[row]: row_off[row] + row_cost[row]]
+                    J = (ent & 0x1FFFFFFF).astype(np.int64)
+                    h0 = (ent >> 29) & 1
+                    h1 = (ent >> 30) & 1
+                    m0 = PU.gpu_mask_row(gout, inp, b, g * G + kg * hpw, I)
+                    m1 = PU.gpu_mask_row(gout, inp, b, g * G + kg * hpw + 1, I)
+                    assert J.tolist() == np.nonzero(m0 | m1)[0].tolist()
+                    assert np.array_equal(h0.astype(bool), m0[J]) and np.array_equal(h1.astype(bool), m1[J])
+                    checked += 1
+    assert checked > 50
+
+
 def test_plan_then_run_equals_prefill():
     # ea_hybrid_attn_plan + ea_hybrid_attn_run is the one-call prefill, and a
     # second run over the same plan gives the same result.

@@ -92,6 +92,28 @@ def test_xa_four_reduced_rows_per_block(B, S):
     assert stats["rows"] > 40
 
 
+@pytest.mark.parametrize("sink,window", [(0, 1), (0, 128), (5000, 64), (1, 2)])
+def test_ssa_degenerate_sink_window(sink, window):
+    # Window 1 keeps only the diagonal key; a sink longer than the sequence
+    # makes SSA equal to FA; sink 0 leaves the window alone.
+    cfg = _small(name=f"ssa-s{sink}-w{window}", seqlens=(1000, 128, 3),
+                 modes=((MODE_SSA, MODE_FA),), ssa_sink=sink, ssa_window=window)
+    inp = make_inputs(cfg)
+    _full_check(inp, f"ssa sink {sink} window {window}")
+
+
+def test_xa_tiny_tau():
+    # tau = 1/1000: the top-mass prefix is a single block, so each mask row
+    # is that block plus the forced sink and diagonal blocks.
+    cfg = _small(name="xa-tiny-tau", seqlens=(2048, 640), modes=((MODE_XA, MODE_XA),),
+                 tau_num=1, tau_den=1000, needle_layout="clustered", needle_blocks_per_64k=512)
+    inp = make_inputs(cfg)
+    gout, masks, stats = _full_check(inp, "xa tau 1/1000")
+    nrows = int(PU.qb_prefix(inp["seqlens"], cfg.block)[-1]) * cfg.num_q_heads
+    rc = gout["row_count"][:nrows]
+    assert (rc >= 1).all() and (rc <= 3).all()
+
+
 def _all_fa(inp):
     inp1 = dict(inp)
     inp1["modes"] = np.zeros_like(inp["modes"])

@@ -35,11 +35,15 @@
 //                 inside each 32-key group of V^T is permuted (bits 2 and 3 of
 //                 the key index swapped) when V is transposed, so the registers
 //                 of P^T line up with the MFMA K index with no data movement.
-// Softmax: exp2 with the scale c*log2(e) folded into one FMA; the reference
-// max is shared by both half-waves (v_permlane32_swap, no LDS) and moves only
-// when a row max exceeds it by more than 2^8 in the exp2 domain, so O and l
-// are rescaled rarely; P stays at most 2^8, far inside the range of bf16 and
-// fp32, and keeps their relative precision.
+// Softmax: exp2 with the scale c*log2(e) folded into one FMA against a lazy
+// reference max, shared by both half-waves (v_permlane32_swap, no LDS).
+// Once every row of the wave has a finite reference, a tile's row maxima are
+// not formed at all: P is computed straight away and each lane's sum of its
+// P values, which bounds every one of them, decides whether the tile must be
+// redone on the exact path.  That path forms the row maxima and moves the
+// reference only when a row max exceeds it by more than 2^8 in the exp2
+// domain, so O and l are rescaled rarely.  P stays at most 2^14, far inside
+// the range of bf16 and fp32, and keeps their relative precision.
 #include "ea_device.h"
 
 namespace ea {
@@ -308,41 +312,55 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
           sacc[kt][r] = ok ? sacc[kt][r] : -INFINITY;
         }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = halves_max(mx);
-    // The reference max mrun moves only when some row max of the wave
-    // exceeds it by more than 2^8 in the exp2 domain (or is its first finite
-    // value); otherwise P = exp2(c (s - mrun)) stays below 256 and neither O
-    // nor l needs rescaling.  l and O always refer to the same mrun.
-    rescale = __any((mx - mrun) * C2 > 8.0f);
-    if (rescale) {
-      const float mnew = fmaxf(mrun, mx);
-      alpha = __builtin_amdgcn_exp2f((mrun - ((mnew == -INFINITY) ? 0.f : mnew)) * C2);
-      mrun = mnew;
-    }
-    const float mb = ((mrun == -INFINITY) ? 0.f : mrun) * C2;
-    // Row sum in fp32 (the bf16 copy of P only feeds the PV MFMA; summing the
-    // rounded copy would cost the LSE up to 2^-9 relative on short rows).
+    // P = exp2(c s - c m) in fp32, its lane sum, and the bf16 copy for the PV
+    // MFMA (the row sum stays in fp32: summing the rounded copy would cost the
+    // LSE up to 2^-9 relative on short rows).
     float psum = 0.f;
+    auto exps = [&](float mb, bool issue) __attribute__((always_inline)) {
+      psum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
-      f32x8 p0, p1;
+      for (int kt = 0; kt < C::NKT; ++kt) {
+        f32x8 p0, p1;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p0[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], C2, -mb));
-        p1[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 + r], C2, -mb));
-        psum += p0[r] + p1[r];
+        for (int r = 0; r < 8; ++r) {
+          p0[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], C2, -mb));
+          p1[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 + r], C2, -mb));
+          psum += p0[r] + p1[r];
+        }
+        pb[kt][0] = __builtin_convertvector(p0, bf16x8);
+        pb[kt][1] = __builtin_convertvector(p1, bf16x8);
+        if (issue) {
+          dma_k_part(kt, C::NKT);
+          dma_v_part(kt, C::NKT);
+        }
       }
-      pb[kt][0] = __builtin_convertvector(p0, bf16x8);
-      pb[kt][1] = __builtin_convertvector(p1, bf16x8);
-      if (dma) {
-        dma_k_part(kt, C::NKT);
-        dma_v_part(kt, C::NKT);
+    };
+    // Fast path: every row of the wave has a finite reference max mrun.  A
+    // lane sum above 2^14 means some P exceeded 2^8, i.e. a row max rose by
+    // more than 2^8 in the exp2 domain: the wave redoes the tile below.  The
+    // sum is +inf, never NaN, if an exponential overflows.
+    rescale = false;
+    const bool cold = __any(mrun == -INFINITY);
+    if (__builtin_expect(!cold, 1)) exps(mrun * C2, dma);
+    if (__builtin_expect(cold || __any(psum > 16384.f), 0)) {
+      // Exact path: row maxima of the tile; the reference max moves only when
+      // one exceeds it by more than 2^8 in the exp2 domain (or is its first
+      // finite value).  l and O always refer to the same mrun.
+      asm volatile("");
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+      mx = halves_max(mx);
+      rescale = __any((mx - mrun) * C2 > 8.0f);
+      if (rescale) {
+        const float mnew = fmaxf(mrun, mx);
+        alpha = __builtin_amdgcn_exp2f((mrun - ((mnew == -INFINITY) ? 0.f : mnew)) * C2);
+        mrun = mnew;
       }
+      // The DMA share went out with the fast path unless it was skipped.
+      exps(((mrun == -INFINITY) ? 0.f : mrun) * C2, dma && cold);
     }
     lrun = (rescale ? lrun * alpha : lrun) + psum;
   };

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from synth import get_config, make_inputs, MODE_FA, MODE_SSA, MODE_XA
+from synth.generate import bf16_bits_to_f32, f32_to_bf16_bits
 import parity_utils as PU
 
 pytestmark = pytest.mark.gpu
@@ -215,6 +216,31 @@ def test_plan_then_run_equals_prefill():
         o = layer.o.float().cpu().numpy().astype(np.float64)
         lse = layer.lse.cpu().numpy().astype(np.float64)
         assert np.array_equal(o, ref["o"]) and np.array_equal(lse, ref["lse"])
+
+
+def test_rising_and_overflowing_scores():
+    # Keys scaled up along each sequence make the row max rise tile after
+    # tile, and a few spike keys aligned with a third of the queries score so
+    # far above the running max that exp2 overflows against it: both cases
+    # must leave the fast softmax path for the exact one and still match.
+    cfg = _small(name="spikes", seqlens=(1024, 640), modes=((MODE_FA, MODE_SSA), (MODE_XA, MODE_FA)))
+    inp = make_inputs(cfg)
+    rng = np.random.Generator(np.random.PCG64(5))
+    d = cfg.head_dim
+    cu = inp["cu_seqlens"]
+    T = int(cu[-1])
+    kf = bf16_bits_to_f32(inp["k"]).copy()
+    qf = bf16_bits_to_f32(inp["q"]).copy()
+    for b in range(len(inp["seqlens"])):
+        L = int(cu[b + 1] - cu[b])
+        kf[cu[b]:cu[b + 1]] *= (1.0 + 3.0 * np.arange(L, dtype=np.float32) / L)[:, None, None]
+    u = rng.standard_normal(d).astype(np.float32)
+    u *= np.float32(np.sqrt(d) / np.linalg.norm(u))
+    kf[rng.choice(T, size=12, replace=False)] = 12.0 * u
+    qf[0::3] += 2.0 * u
+    inp["k"] = f32_to_bf16_bits(kf)
+    inp["q"] = f32_to_bf16_bits(qf)
+    _full_check(inp, "rising and overflowing scores")
 
 
 def test_deterministic():

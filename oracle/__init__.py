@@ -11,8 +11,10 @@ Modules
   attention  masked softmax attention for FA / SSA / XA heads (Eqs. 1-3)
   xa         antidiagonal block scoring and the top-mass block selector
   ratios     Omega_MSR / Omega_ESR and the per-head pruning rate rho (Eqs. 4-5)
+  router     the Attention Router's inference pass: boundary pooling of the
+             key states, Task MLP, Router MLP, arg max
 
 Parity status of each function is stated in its module header.
 """
 
-from . import attention, xa, ratios  # noqa: F401
+from . import attention, xa, ratios, router  # noqa: F401

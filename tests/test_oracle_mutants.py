@@ -92,3 +92,64 @@ def test_mutant_ssa_pairs_sink_double_counted(monkeypatch):
     monkeypatch.setattr(OR, "ssa_kept_pairs", double)
     with pytest.raises(AssertionError):
         TR.test_ssa_pairs_brute_and_closed_form(300, 7, 40)
+
+
+# ---- router -------------------------------------------------------------
+
+import test_oracle_router as TRT
+from oracle import router as ORT
+
+
+def test_mutant_router_pools_every_token(monkeypatch):
+    monkeypatch.setattr(ORT, "boundary_positions", lambda L, head=100, tail=100: np.arange(int(L)))
+    with pytest.raises(AssertionError):
+        TRT.test_pool_quadratic_closed_form(333)
+
+
+def test_mutant_router_counts_overlap_twice(monkeypatch):
+    def twice(L, head=100, tail=100):
+        L = int(L)
+        return np.concatenate([np.arange(min(head, L)), np.arange(max(L - tail, 0), L)])
+    monkeypatch.setattr(ORT, "boundary_positions", twice)
+    with pytest.raises(AssertionError):
+        TRT.test_pool_quadratic_closed_form(150)
+
+
+def test_mutant_router_concat_swapped(monkeypatch):
+    def swapped(pooled, w):
+        f = {n: np.asarray(a, dtype=np.float64) for n, a in w.items()}
+        x = np.asarray(pooled, dtype=np.float64)
+        z_task = ORT.relu(x @ f["w1"] + f["b1"]) @ f["w2"] + f["b2"]
+        h = ORT.relu(np.concatenate([z_task, x], axis=-1) @ f["w3"] + f["b3"])   # planted
+        return h @ f["w4"] + f["b4"]
+    monkeypatch.setattr(ORT, "router_logits", swapped)
+    with pytest.raises(AssertionError):
+        TRT.test_worked_example()
+
+
+def test_mutant_router_transposed_w3(monkeypatch):
+    orig = ORT.router_logits
+
+    def transposed(pooled, w):
+        w = dict(w)
+        w["w3"] = np.asarray(w["w3"]).T                                         # planted
+        return orig(pooled, w)
+    monkeypatch.setattr(ORT, "router_logits", transposed)
+    with pytest.raises(AssertionError):
+        TRT.test_worked_example()
+
+
+def test_mutant_router_no_relu(monkeypatch):
+    monkeypatch.setattr(ORT, "relu", lambda x: x)                               # planted
+    with pytest.raises(AssertionError):
+        TRT.test_worked_example()
+
+
+def test_mutant_router_ties_to_sparse(monkeypatch):
+    def ties_sparse(logits, retrieval_mode, sparse_mode):
+        z = np.asarray(logits)
+        r = (z[..., 1] >= z[..., 0]).astype(np.int64)                          # planted
+        return np.where(r == 1, sparse_mode, retrieval_mode).astype(np.uint8)
+    monkeypatch.setattr(ORT, "decide", ties_sparse)
+    with pytest.raises(AssertionError):
+        TRT.test_decision_mapping_and_ties()

@@ -11,7 +11,8 @@ default workload is the Llama-3.1-8B-shaped FA-SSA layer at 64K tokens
 Reported beside the throughput: ms per layer, tokens/s, effective TFLOP/s
 (4 B^2 d per computed tile) and pair-level TFLOP/s (4 d per attended pair),
 the speedup over the same kernel with every head in FA mode, the roofline of
-the attention kernel, and the fp64 oracle timed on the host cores.
+the attention kernel, the latency of the attention router (ea_route_heads,
+off the hot path) and the fp64 oracle timed on the host cores.
 """
 
 import argparse
@@ -275,6 +276,16 @@ def main():
     rat = layer.ratios(cfg.sparse_mode)
     traffic = traffic_record(cfg.name)
 
+    # The attention router (off the hot path, reported beside it): modes for
+    # every (sequence, KV head) from the boundary-pooled keys, seeded random
+    # weights of the pages' shape (hidden 4 d), into a buffer of its own.
+    from hybrid_sparse_full_amd.layer import Router
+    from synth.router_weights import make_router_weights
+    router = Router(make_router_weights(D, 4 * D, seed=1), device=dev)
+    routed = torch.empty(desc.num_seqs * desc.num_kv_heads, dtype=torch.uint8, device=dev)
+    _, router_ms, _ = time_steps(lambda: router(desc, k, layer.cu, 0, cfg.sparse_mode, routed),
+                                 max(a.steps, 20), a.warmup)
+
     speedup = None
     allfa_ms = None
     if not a.no_all_fa:
@@ -322,6 +333,13 @@ def main():
         "omega_msr": round(float(rat["msr"][-1]), 6),
         "omega_esr": round(float(rat["esr"][-1]), 6),
         "omega_esr_pair_weighted": round(rat["esr_pairs"], 6),
+        "router": {
+            "ms": round(router_ms, 4),
+            "heads_routed": desc.num_seqs * desc.num_kv_heads,
+            "pooled_tokens_per_sequence": 200,
+            "hidden": 4 * D,
+            "weights": "seeded random (no trained router weights)",
+        },
         "roofline": {
             "kernel": "k_attn (fused hybrid attention)",
             "bound": "mfma",

@@ -261,6 +261,33 @@ ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, co
                             workspace_bytes, stream);
 }
 
+ea_status ea_route_heads(const ea_attn_desc* desc, const ea_router_desc* router,
+                         const void* k_dev, const int32_t* cu_seqlens_dev,
+                         uint8_t retrieval_mode, uint8_t sparse_mode, uint8_t* modes_out_dev,
+                         float* logits_out_dev, void* stream) {
+  EaDims d;
+  ea_status st = make_dims(desc, &d);
+  if (st != EA_OK) return st;
+  if (!router || !cu_seqlens_dev) return EA_ERR_INVALID_ARG;
+  const ea_router_desc& w = *router;
+  if (w.hidden < 1 || w.hidden > 1024 || w.pool_head < 0 || w.pool_tail < 0)
+    return EA_ERR_INVALID_ARG;
+  if (retrieval_mode > 2 || sparse_mode > 2) return EA_ERR_INVALID_ARG;
+  if (d.nseq == 0) return EA_OK;
+  if (!modes_out_dev || !w.w1 || !w.b1 || !w.w2 || !w.b2 || !w.w3 || !w.b3 || !w.w4 || !w.b4)
+    return EA_ERR_INVALID_ARG;
+  const void* wp[8] = {w.w1, w.b1, w.w2, w.b2, w.w3, w.b3, w.w4, w.b4};
+  for (const void* p : wp)
+    if ((uintptr_t)p & 3u) return EA_ERR_INVALID_ARG;
+  if (d.T > 0 && !k_dev) return EA_ERR_INVALID_ARG;
+  if (misaligned(k_dev) || ((uintptr_t)logits_out_dev & 3u)) return EA_ERR_INVALID_ARG;
+  if ((int64_t)d.nseq * d.Hkv > 0x7fffffff) return EA_ERR_UNSUPPORTED;
+  if (launch_route(d, w, (const uint16_t*)k_dev, cu_seqlens_dev, retrieval_mode, sparse_mode,
+                   modes_out_dev, logits_out_dev, (hipStream_t)stream) != hipSuccess)
+    return EA_ERR_HIP;
+  return EA_OK;
+}
+
 ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu, const uint8_t* modes,
                              uint8_t sparse_mode, const int64_t* xa_pairs, double* msr_out,
                              double* esr_out, double* rho_out, double* esr_pw_out) {

@@ -76,6 +76,9 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v
                            const WsLayout& L, hipStream_t st);
 hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint8_t* modes, const SeqMeta& m, void* ws,
                             const WsLayout& L, uint16_t* o, float* lse, hipStream_t st);
+hipError_t launch_route(const EaDims& d, const ea_router_desc& w, const uint16_t* k,
+                        const int32_t* cu, uint8_t retrieval_mode, uint8_t sparse_mode,
+                        uint8_t* modes, float* logits, hipStream_t st);
 
 // ---- helpers usable on host and device ----
 __host__ __device__ inline int64_t tri64(int64_t n) { return n * (n + 1) / 2; }

@@ -29,8 +29,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libea.so")
 EXPORTS = (
     "ea_workspace_bytes", "ea_mask_rows", "ea_mask_words", "ea_workspace_offset",
     "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_hybrid_attn_plan", "ea_hybrid_attn_run",
-    "ea_sparsity_ratios", "ea_status_string",
+    "ea_sparsity_ratios", "ea_route_heads", "ea_status_string",
 )
+
+# Router weight arrays in ea_router_desc order: Task MLP (w1, b1, w2, b2),
+# Router MLP (w3, b3, w4, b4); fp32, row-major [in][out].
+ROUTER_WEIGHTS = ("w1", "b1", "w2", "b2", "w3", "b3", "w4", "b4")
 
 
 class EaError(RuntimeError):
@@ -52,6 +56,12 @@ class AttnDesc(ctypes.Structure):
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class RouterDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ROUTER_WEIGHTS] + [
+        ("hidden", ctypes.c_int32), ("pool_head", ctypes.c_int32), ("pool_tail", ctypes.c_int32),
+    ]
 
 
 _lib = None
@@ -86,6 +96,9 @@ def lib():
     L.ea_hybrid_attn_run.restype = ctypes.c_int
     L.ea_sparsity_ratios.argtypes = [D, P, P, ctypes.c_uint8, P, P, P, P, P]
     L.ea_sparsity_ratios.restype = ctypes.c_int
+    L.ea_route_heads.argtypes = [D, ctypes.POINTER(RouterDesc), P, P, ctypes.c_uint8, ctypes.c_uint8,
+                                 P, P, P]
+    L.ea_route_heads.restype = ctypes.c_int
     L.ea_status_string.argtypes = [ctypes.c_int]
     L.ea_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -183,3 +196,13 @@ def ea_sparsity_ratios(desc, cu_seqlens_host, modes_host, sparse_mode, xa_pairs_
         _ptr(esr_pair_weighted_out))
     if st != EA_OK:
         raise EaError(st, "ea_sparsity_ratios")
+
+
+def ea_route_heads(desc, router_desc, k, cu_seqlens, retrieval_mode, sparse_mode, modes_out,
+                   logits_out=None, stream=None):
+    st = lib().ea_route_heads(
+        ctypes.byref(desc), ctypes.byref(router_desc) if router_desc is not None else None,
+        _ptr(k), _ptr(cu_seqlens), int(retrieval_mode), int(sparse_mode), _ptr(modes_out),
+        _ptr(logits_out), _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_route_heads")

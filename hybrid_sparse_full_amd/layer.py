@@ -2,8 +2,10 @@
 
 `HybridPrefill` owns the workspaces and output buffers (torch tensors, so
 torch's caching allocator provides device memory and streams) and calls the
-two device entry points in order: ea_xa_block_select when some head is XA,
-then ea_hybrid_attn_prefill.  All arithmetic happens inside libea.so.
+device entry points in order: optionally ea_route_heads (modes written on the
+device by the attention router), ea_xa_block_select when some head can be
+XA, then ea_hybrid_attn_prefill.  `Router` holds the router weights on the
+device.  All arithmetic happens inside libea.so.
 """
 
 import math
@@ -25,21 +27,52 @@ def make_desc(*, num_seqs, total_tokens, max_seqlen, num_q_heads, num_kv_heads, 
                       int(xa_tau[1]))
 
 
+class Router:
+    """The attention router's weights on the device and the ea_router_desc
+    that points at them.  `weights` maps w1, b1, w2, b2, w3, b3, w4, b4 to
+    arrays of shape [d, H], [H], [H, d], [d], [2d, H], [H], [H, 2], [2]."""
+
+    def __init__(self, weights, device="cuda", pool_head=100, pool_tail=100):
+        self.device = torch.device(device)
+        self.t = {n: torch.from_numpy(np.ascontiguousarray(weights[n], dtype=np.float32)).to(self.device)
+                  for n in E.ROUTER_WEIGHTS}
+        self.hidden = int(self.t["w1"].shape[1])
+        self.desc = E.RouterDesc(*[self.t[n].data_ptr() for n in E.ROUTER_WEIGHTS],
+                                 self.hidden, int(pool_head), int(pool_tail))
+
+    def __call__(self, attn_desc, k, cu_seqlens, retrieval_mode, sparse_mode, modes_out,
+                 logits_out=None, stream=None):
+        E.ea_route_heads(attn_desc, self.desc, k, cu_seqlens, retrieval_mode, sparse_mode,
+                         modes_out, logits_out, stream)
+
+
 class HybridPrefill:
     """One layer's buffers for a fixed descriptor.
 
     cu_seqlens and modes are given as host numpy arrays; they are copied to
-    the device once here (the C ABI reads them on the device).
+    the device once here (the C ABI reads them on the device).  With
+    modes=None the modes are left to `route` (the attention router writes
+    them on the device); `mode_set` = (retrieval mode, sparse mode) then says
+    which modes it may write.
     """
 
-    def __init__(self, desc, cu_seqlens, modes, device="cuda", block_mass=False):
+    def __init__(self, desc, cu_seqlens, modes, device="cuda", block_mass=False, mode_set=None):
         self.desc = desc
         self.device = torch.device(device)
         self.cu_host = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
-        self.modes_host = np.ascontiguousarray(modes, dtype=np.uint8)
         self.cu = torch.from_numpy(self.cu_host).to(self.device)
-        self.modes = torch.from_numpy(self.modes_host.reshape(-1)).to(self.device)
-        self.has_xa = bool((self.modes_host == E.EA_MODE_XA).any())
+        self.mode_set = tuple(int(x) for x in mode_set) if mode_set is not None else None
+        if modes is None:
+            if self.mode_set is None:
+                raise ValueError("modes=None needs mode_set=(retrieval_mode, sparse_mode)")
+            self.modes_host = None
+            self.modes = torch.zeros(desc.num_seqs * desc.num_kv_heads, dtype=torch.uint8,
+                                     device=self.device)
+            self.has_xa = E.EA_MODE_XA in self.mode_set
+        else:
+            self.modes_host = np.ascontiguousarray(modes, dtype=np.uint8)
+            self.modes = torch.from_numpy(self.modes_host.reshape(-1)).to(self.device)
+            self.has_xa = bool((self.modes_host == E.EA_MODE_XA).any())
         T, Hq, D = desc.total_tokens, desc.num_q_heads, desc.head_dim
         self.o = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=self.device)
         self.lse = torch.empty((Hq, T), dtype=torch.float32, device=self.device)
@@ -58,6 +91,17 @@ class HybridPrefill:
             if block_mass:
                 self.block_mass = torch.zeros((self.rows, self.maxqb), dtype=torch.float32,
                                               device=self.device)
+
+    def route(self, router, k, logits_out=None, stream=None):
+        """Modes from the attention router, written on the device."""
+        if self.mode_set is None:
+            raise ValueError("route() needs mode_set=(retrieval_mode, sparse_mode)")
+        router(self.desc, k, self.cu, self.mode_set[0], self.mode_set[1], self.modes,
+               logits_out, stream)
+
+    def device_modes(self):
+        """The modes the kernels read, copied back to the host [num_seqs, Hkv]."""
+        return self.modes.cpu().numpy().reshape(self.desc.num_seqs, self.desc.num_kv_heads)
 
     def select(self, q, k, stream=None):
         E.ea_xa_block_select(self.desc, q, k, self.cu, self.modes, self.mask, self.row_count,
@@ -83,7 +127,8 @@ class HybridPrefill:
 
     def ratios(self, sparse_mode):
         """Omega_MSR / Omega_ESR / rho on the host (needs the XA pair counts)."""
-        nseq, hkv = self.modes_host.shape
+        modes_host = self.modes_host if self.modes_host is not None else self.device_modes()
+        nseq, hkv = modes_host.shape
         msr = np.zeros(nseq + 1)
         esr = np.zeros(nseq + 1)
         rho = np.zeros(nseq * hkv)
@@ -91,7 +136,7 @@ class HybridPrefill:
         pairs = None
         if self.has_xa:
             pairs = np.ascontiguousarray(self.xa_pairs.cpu().numpy())
-        E.ea_sparsity_ratios(self.desc, self.cu_host, self.modes_host, sparse_mode, pairs,
+        E.ea_sparsity_ratios(self.desc, self.cu_host, np.ascontiguousarray(modes_host), sparse_mode, pairs,
                              msr, esr, rho, pw)
         return dict(msr=msr, esr=esr, rho=rho.reshape(nseq, hkv), esr_pairs=float(pw[0]))
 

@@ -205,6 +205,59 @@ ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu_seqlens
                              double* rho_out, double* esr_pair_weighted_out);
 
 /*
+ * Attention Router, inference pass (English paper-reading notes, 03 Method,
+ * Figure 3 (b)(c) and the configuration taken from Appendix C.1; Chinese
+ * notes, 04 Method).  For every (sequence b, KV head g):
+ *   x  = mean of k[b, t, g, :] over the boundary tokens t of the sequence:
+ *        the first pool_head and the last pool_tail, each token once (a
+ *        sequence shorter than pool_head + pool_tail pools all its tokens,
+ *        an empty one gives x = 0);
+ *   u  = relu(x W1 + b1) W2 + b2                       (Task MLP, d -> H -> d)
+ *   z  = relu([x, u] W3 + b3) W4 + b4                  (Router MLP, 2d -> H -> 2)
+ *   modes_out[b, g] = z[1] > z[0] ? sparse_mode : retrieval_mode
+ * (r = 0 is FA / the retrieval mode, r = 1 the sparse mode; ties go to the
+ * retrieval mode).  The pages give pool_head = pool_tail = 100 and
+ * H = 4 d; the weights are shared by the KV heads of the layer.  The pages
+ * leave the pooling operator and the activation open: mean and ReLU here.
+ *
+ * router: host struct of device pointers to fp32 arrays, row-major [in][out]:
+ *   w1 [d][H], b1 [H], w2 [H][d], b2 [d], w3 [2d][H], b3 [H], w4 [H][2],
+ *   b4 [2]; hidden = H in 1..1024; pool_head, pool_tail >= 0.
+ * desc: the layer descriptor (num_seqs, total_tokens, max_seqlen,
+ *   num_kv_heads and head_dim are used; the whole descriptor must be valid).
+ * k_dev: bf16 [total_tokens, num_kv_heads, head_dim], 16-byte aligned.
+ * cu_seqlens_dev: int32 [num_seqs + 1]; values are clamped into
+ *   [0, total_tokens] and each length to max_seqlen, so reads stay in bounds
+ *   whatever it holds.
+ * retrieval_mode, sparse_mode: mode codes 0..2 written for r = 0 and r = 1.
+ * modes_out_dev: uint8 [num_seqs, num_kv_heads], written (device memory; can
+ *   be passed straight to ea_xa_block_select / ea_hybrid_attn_prefill).
+ * logits_out_dev: fp32 [num_seqs, num_kv_heads, 2] or NULL.
+ * The caller owns every buffer; the call allocates nothing and needs no
+ * workspace.  Returns EA_ERR_INVALID_ARG / EA_ERR_UNSUPPORTED before any
+ * launch on bad arguments, EA_ERR_HIP if the launch fails.  Asynchronous on
+ * `stream`.
+ */
+typedef struct {
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+  const float* w3;
+  const float* b3;
+  const float* w4;
+  const float* b4;
+  int32_t hidden;
+  int32_t pool_head;
+  int32_t pool_tail;
+} ea_router_desc;
+
+ea_status ea_route_heads(const ea_attn_desc* desc, const ea_router_desc* router,
+                         const void* k_dev, const int32_t* cu_seqlens_dev,
+                         uint8_t retrieval_mode, uint8_t sparse_mode, uint8_t* modes_out_dev,
+                         float* logits_out_dev, void* stream);
+
+/*
  * Diagnostics: byte offset of a named internal buffer inside the workspace of
  * `op` (for example "tiles", "row_off", "row_cost", "sorted_units" of the
  * prefill work list, "xa_lse" of the selector), or -1 if the name is unknown

@@ -227,3 +227,48 @@ def test_page_fact_ratios_through_c_abi():
     msr, esr, rho, pw = _ratios_c(d, np.array([0, L]), np.array([[MODE_XA, MODE_FA]], np.uint8),
                                   MODE_XA, pairs)
     assert abs(rho[0, 0] - 0.9) < 1e-12 and rho[0, 1] == 0 and msr[0] == 0.5
+
+
+def _router_desc(**kw):
+    base = dict(hidden=512, pool_head=100, pool_tail=100)
+    base.update(kw)
+    return E.RouterDesc(*([FAKE] * len(E.ROUTER_WEIGHTS)), base["hidden"], base["pool_head"],
+                        base["pool_tail"])
+
+
+def test_route_heads_rejects_bad_arguments():
+    L = E.lib()
+    d = desc()
+    ok = dict(k=FAKE, cu=FAKE, rm=MODE_FA, sm=MODE_SSA, modes=FAKE, logits=FAKE)
+
+    def call(rd, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.ea_route_heads(ctypes.byref(d), ctypes.byref(rd) if rd is not None else None,
+                                a["k"], a["cu"], a["rm"], a["sm"], a["modes"], a["logits"], None)
+
+    bad = E.EA_ERR_INVALID_ARG
+    assert call(None) == bad
+    assert call(_router_desc(hidden=0)) == bad
+    assert call(_router_desc(hidden=1025)) == bad
+    assert call(_router_desc(pool_head=-1)) == bad
+    assert call(_router_desc(pool_tail=-1)) == bad
+    assert call(_router_desc(), rm=3) == bad
+    assert call(_router_desc(), sm=7) == bad
+    assert call(_router_desc(), cu=None) == bad
+    assert call(_router_desc(), modes=None) == bad
+    assert call(_router_desc(), k=None) == bad
+    assert call(_router_desc(), k=FAKE + 2) == bad
+    assert call(_router_desc(), logits=FAKE + 2) == bad
+    rd = _router_desc()
+    rd.w3 = None
+    assert call(rd) == bad
+    rd = _router_desc()
+    rd.b4 = FAKE + 1
+    assert call(rd) == bad
+    # A bad layer descriptor is rejected the same way as by the other calls.
+    d = desc(head_dim=96)
+    assert call(_router_desc()) == E.EA_ERR_UNSUPPORTED
+    # No sequence: nothing to do, nothing touched.
+    d = desc(num_seqs=0, total_tokens=0, max_seqlen=0)
+    assert call(_router_desc(), modes=None, k=None) == E.EA_OK

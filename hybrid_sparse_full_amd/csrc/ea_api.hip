@@ -270,7 +270,7 @@ ea_status ea_route_heads(const ea_attn_desc* desc, const ea_router_desc* router,
   if (st != EA_OK) return st;
   if (!router || !cu_seqlens_dev) return EA_ERR_INVALID_ARG;
   const ea_router_desc& w = *router;
-  if (w.hidden < 1 || w.hidden > 1024 || w.pool_head < 0 || w.pool_tail < 0)
+  if (w.hidden < 4 || w.hidden > 1024 || w.hidden % 4 || w.pool_head < 0 || w.pool_tail < 0)
     return EA_ERR_INVALID_ARG;
   if (retrieval_mode > 2 || sparse_mode > 2) return EA_ERR_INVALID_ARG;
   if (d.nseq == 0) return EA_OK;
@@ -279,6 +279,7 @@ ea_status ea_route_heads(const ea_attn_desc* desc, const ea_router_desc* router,
   const void* wp[8] = {w.w1, w.b1, w.w2, w.b2, w.w3, w.b3, w.w4, w.b4};
   for (const void* p : wp)
     if ((uintptr_t)p & 3u) return EA_ERR_INVALID_ARG;
+  if (misaligned(w.w1) || misaligned(w.w2) || misaligned(w.w3)) return EA_ERR_INVALID_ARG;
   if (d.T > 0 && !k_dev) return EA_ERR_INVALID_ARG;
   if (misaligned(k_dev) || ((uintptr_t)logits_out_dev & 3u)) return EA_ERR_INVALID_ARG;
   if ((int64_t)d.nseq * d.Hkv > 0x7fffffff) return EA_ERR_UNSUPPORTED;

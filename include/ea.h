@@ -222,7 +222,8 @@ ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu_seqlens
  *
  * router: host struct of device pointers to fp32 arrays, row-major [in][out]:
  *   w1 [d][H], b1 [H], w2 [H][d], b2 [d], w3 [2d][H], b3 [H], w4 [H][2],
- *   b4 [2]; hidden = H in 1..1024; pool_head, pool_tail >= 0.
+ *   b4 [2]; hidden = H, a multiple of 4 in 4..1024; w1, w2 and w3 16-byte
+ *   aligned, the biases and w4 4-byte aligned; pool_head, pool_tail >= 0.
  * desc: the layer descriptor (num_seqs, total_tokens, max_seqlen,
  *   num_kv_heads and head_dim are used; the whole descriptor must be valid).
  * k_dev: bf16 [total_tokens, num_kv_heads, head_dim], 16-byte aligned.

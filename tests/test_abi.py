@@ -251,6 +251,8 @@ def test_route_heads_rejects_bad_arguments():
     assert call(None) == bad
     assert call(_router_desc(hidden=0)) == bad
     assert call(_router_desc(hidden=1025)) == bad
+    assert call(_router_desc(hidden=1028)) == bad
+    assert call(_router_desc(hidden=6)) == bad
     assert call(_router_desc(pool_head=-1)) == bad
     assert call(_router_desc(pool_tail=-1)) == bad
     assert call(_router_desc(), rm=3) == bad
@@ -265,6 +267,9 @@ def test_route_heads_rejects_bad_arguments():
     assert call(rd) == bad
     rd = _router_desc()
     rd.b4 = FAKE + 1
+    assert call(rd) == bad
+    rd = _router_desc()
+    rd.w2 = FAKE + 4
     assert call(rd) == bad
     # A bad layer descriptor is rejected the same way as by the other calls.
     d = desc(head_dim=96)

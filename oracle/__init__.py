@@ -13,8 +13,10 @@ Modules
   ratios     Omega_MSR / Omega_ESR and the per-head pruning rate rho (Eqs. 4-5)
   router     the Attention Router's inference pass: boundary pooling of the
              key states, Task MLP, Router MLP, arg max
+  decode     one decode step: the newest token of each sequence over the
+             keys its head's mode keeps
 
 Parity status of each function is stated in its module header.
 """
 
-from . import attention, xa, ratios, router  # noqa: F401
+from . import attention, xa, ratios, router, decode  # noqa: F401

@@ -153,3 +153,30 @@ def test_mutant_router_ties_to_sparse(monkeypatch):
     monkeypatch.setattr(ORT, "decide", ties_sparse)
     with pytest.raises(AssertionError):
         TRT.test_decision_mapping_and_ties()
+
+
+# ---- decode -------------------------------------------------------------
+
+import test_oracle_decode as TD
+from oracle import decode as OD
+
+
+def test_mutant_decode_xa_as_ssa(monkeypatch):
+    src = OD.decode
+
+    def decode_xa_as_ssa(q_new, k, v, cu, modes, **kw):
+        m = np.where(np.asarray(modes) == OD.MODE_XA, OD.MODE_SSA, modes)       # planted
+        return src(q_new, k, v, cu, m, **kw)
+    monkeypatch.setattr(OD, "decode", decode_xa_as_ssa)
+    with pytest.raises(AssertionError):
+        TD.test_decode_matches_sdpa_on_gathered_keys(4, 16)
+
+
+def test_mutant_decode_query_one_back(monkeypatch):
+    orig = OD.row_attention
+
+    def one_back(q_i, k_seq, v_seq, i, mode, scale, **kw):
+        return orig(q_i, k_seq, v_seq, max(i - 1, 0), mode, scale, **kw)          # planted
+    monkeypatch.setattr(OD, "row_attention", one_back)
+    with pytest.raises(AssertionError):
+        TD.test_zero_query_closed_form(13, 4, 8)

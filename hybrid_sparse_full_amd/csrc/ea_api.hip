@@ -71,6 +71,11 @@ size_t ws_layout(const EaDims& d, int op, WsLayout* L) {
   L->tri_prefix = take(8 * (size_t)(d.nseq + 1));
   L->qb2seq = take(4 * (size_t)d.nqb_max);
   L->scal = take(4 * (size_t)SCAL_COUNT);
+  if (op == EA_OP_DECODE) {
+    L->dec_part = take(4 * (size_t)d.nseq * d.Hq * (size_t)decode_splits(d) * (d.D + 2));
+    L->total = off;
+    return off;
+  }
   if (op == EA_OP_XA_SELECT) {
     const size_t pairs = (size_t)d.nseq * d.Hq;
     L->xa_pair_bh = take(4 * pairs);
@@ -113,7 +118,7 @@ extern "C" {
 size_t ea_workspace_bytes(const ea_attn_desc* desc, int op) {
   EaDims d;
   if (make_dims(desc, &d) != EA_OK) return 0;
-  if (op != EA_OP_XA_SELECT && op != EA_OP_PREFILL) return 0;
+  if (op != EA_OP_XA_SELECT && op != EA_OP_PREFILL && op != EA_OP_DECODE) return 0;
   WsLayout L;
   return ws_layout(d, op, &L);
 }
@@ -259,6 +264,32 @@ ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, co
   if (st != EA_OK) return st;
   return ea_hybrid_attn_run(desc, q_dev, modes_dev, o_out_dev, lse_out_dev, workspace_dev,
                             workspace_bytes, stream);
+}
+
+ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
+                                const void* v_dev, const int32_t* cu_seqlens_dev,
+                                const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
+                                void* workspace_dev, size_t workspace_bytes, void* stream) {
+  EaDims d;
+  ea_status st = make_dims(desc, &d);
+  if (st != EA_OK) return st;
+  if (d.G > 16) return EA_ERR_UNSUPPORTED;
+  if (!cu_seqlens_dev || !modes_dev) return EA_ERR_INVALID_ARG;
+  if (d.nseq > 0 && (!q_dev || !o_out_dev || !lse_out_dev)) return EA_ERR_INVALID_ARG;
+  if (d.T > 0 && (!k_dev || !v_dev)) return EA_ERR_INVALID_ARG;
+  if (misaligned(q_dev) || misaligned(k_dev) || misaligned(v_dev) || misaligned(o_out_dev) ||
+      ((uintptr_t)lse_out_dev & 3u))
+    return EA_ERR_INVALID_ARG;
+  if (d.nseq > 65535 || d.Hkv > 65535) return EA_ERR_UNSUPPORTED;
+  WsLayout L;
+  const size_t need = ws_layout(d, EA_OP_DECODE, &L);
+  if (!workspace_dev || workspace_bytes < need) return EA_ERR_WORKSPACE;
+  if (d.nseq == 0) return EA_OK;
+  if (launch_decode(d, (const uint16_t*)q_dev, (const uint16_t*)k_dev, (const uint16_t*)v_dev,
+                    cu_seqlens_dev, modes_dev, (char*)workspace_dev + L.dec_part,
+                    (uint16_t*)o_out_dev, lse_out_dev, (hipStream_t)stream) != hipSuccess)
+    return EA_ERR_HIP;
+  return EA_OK;
 }
 
 ea_status ea_route_heads(const ea_attn_desc* desc, const ea_router_desc* router,

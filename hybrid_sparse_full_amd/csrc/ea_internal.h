@@ -56,6 +56,8 @@ struct WsLayout {
   size_t xa_pair_bh, xa_pair_items, xa_lse;
   // prefill
   size_t kvp, unit_cost, row_cost, row_off, hist, cursor, sorted_units, tiles;
+  // decode
+  size_t dec_part;
   size_t total;
 };
 
@@ -76,6 +78,12 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v
                            const WsLayout& L, hipStream_t st);
 hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint8_t* modes, const SeqMeta& m, void* ws,
                             const WsLayout& L, uint16_t* o, float* lse, hipStream_t st);
+// Decode: key-set positions per split workgroup, and the split bound.
+constexpr int32_t DEC_SPLIT = 1024;
+inline int32_t decode_splits(const EaDims& d) { return (d.maxL + DEC_SPLIT - 1) / DEC_SPLIT; }
+hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int32_t* cu, const uint8_t* modes, void* ws, uint16_t* o, float* lse,
+                         hipStream_t st);
 hipError_t launch_route(const EaDims& d, const ea_router_desc& w, const uint16_t* k,
                         const int32_t* cu, uint8_t retrieval_mode, uint8_t sparse_mode,
                         uint8_t* modes, float* logits, hipStream_t st);

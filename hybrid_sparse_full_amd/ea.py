@@ -22,6 +22,7 @@ EA_MODE_XA = 2
 
 EA_OP_XA_SELECT = 0
 EA_OP_PREFILL = 1
+EA_OP_DECODE = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libea.so")
 
@@ -29,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libea.so")
 EXPORTS = (
     "ea_workspace_bytes", "ea_mask_rows", "ea_mask_words", "ea_workspace_offset",
     "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_hybrid_attn_plan", "ea_hybrid_attn_run",
-    "ea_sparsity_ratios", "ea_route_heads", "ea_status_string",
+    "ea_sparsity_ratios", "ea_route_heads", "ea_hybrid_attn_decode", "ea_status_string",
 )
 
 # Router weight arrays in ea_router_desc order: Task MLP (w1, b1, w2, b2),
@@ -99,6 +100,8 @@ def lib():
     L.ea_route_heads.argtypes = [D, ctypes.POINTER(RouterDesc), P, P, ctypes.c_uint8, ctypes.c_uint8,
                                  P, P, P]
     L.ea_route_heads.restype = ctypes.c_int
+    L.ea_hybrid_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.ea_hybrid_attn_decode.restype = ctypes.c_int
     L.ea_status_string.argtypes = [ctypes.c_int]
     L.ea_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -206,3 +209,12 @@ def ea_route_heads(desc, router_desc, k, cu_seqlens, retrieval_mode, sparse_mode
         _ptr(logits_out), _stream(stream))
     if st != EA_OK:
         raise EaError(st, "ea_route_heads")
+
+
+def ea_hybrid_attn_decode(desc, q, k, v, cu_seqlens, modes, o_out, lse_out, workspace, stream=None):
+    st = lib().ea_hybrid_attn_decode(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(modes), _ptr(o_out),
+        _ptr(lse_out), _ptr(workspace), _nbytes(workspace) if workspace is not None else 0,
+        _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_hybrid_attn_decode")

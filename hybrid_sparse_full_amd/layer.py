@@ -141,6 +141,28 @@ class HybridPrefill:
         return dict(msr=msr, esr=esr, rho=rho.reshape(nseq, hkv), esr_pairs=float(pw[0]))
 
 
+class HybridDecode:
+    """Buffers of one decode step for a fixed descriptor: the descriptor
+    describes the cache (cu_seqlens over the cached tokens, the current token
+    included); q holds one new query per sequence."""
+
+    def __init__(self, desc, cu_seqlens, modes, device="cuda"):
+        self.desc = desc
+        self.device = torch.device(device)
+        self.cu = torch.from_numpy(np.ascontiguousarray(cu_seqlens, dtype=np.int32)).to(self.device)
+        self.modes = torch.from_numpy(np.ascontiguousarray(modes, dtype=np.uint8).reshape(-1)).to(self.device)
+        nseq, Hq, D = desc.num_seqs, desc.num_q_heads, desc.head_dim
+        self.o = torch.empty((nseq, Hq, D), dtype=torch.bfloat16, device=self.device)
+        self.lse = torch.empty((nseq, Hq), dtype=torch.float32, device=self.device)
+        self.ws = torch.empty(max(1, E.ea_workspace_bytes(desc, E.EA_OP_DECODE)), dtype=torch.uint8,
+                              device=self.device)
+
+    def __call__(self, q, k, v, stream=None):
+        E.ea_hybrid_attn_decode(self.desc, q, k, v, self.cu, self.modes, self.o, self.lse, self.ws,
+                                stream)
+        return self.o, self.lse
+
+
 def bf16_tensor(bits, device):
     """uint16 bf16 bit patterns (numpy) -> torch bfloat16 on `device`."""
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))

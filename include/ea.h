@@ -74,6 +74,7 @@ typedef struct {
 /* Operation codes for ea_workspace_bytes. */
 #define EA_OP_XA_SELECT 0
 #define EA_OP_PREFILL 1
+#define EA_OP_DECODE 2
 
 /*
  * Workspace bytes that `op` needs for `desc`: an upper bound computed from
@@ -203,6 +204,34 @@ ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu_seqlens
                              const uint8_t* modes_host, uint8_t sparse_mode,
                              const int64_t* xa_pairs_host, double* msr_out, double* esr_out,
                              double* rho_out, double* esr_pair_weighted_out);
+
+/*
+ * One decode step of the hybrid-head layer (routing is decided once per
+ * request at prefill and reused for every generated token: English
+ * paper-reading notes, 08 Commentary, the authors' stated limits, item 3).
+ * The k / v cache already holds the current token: sequence b owns cache rows
+ * [cu_seqlens[b], cu_seqlens[b+1]) of length L_b, and its new query (index
+ * L_b - 1) attends, for q-head h of KV head g:
+ *   A = { j <= L_b - 1 }                                         FA and XA
+ *     = { j <= L_b - 1 : j < ssa_sink or L_b - 1 - j < ssa_window }   SSA
+ *   o = sum_{j in A} softmax_j(c <q, k_j>) v_j,  lse = ln sum_{j in A} exp(c <q, k_j>).
+ * XA heads attend every cached key: block selection needs blocks of query
+ * rows, and a decode step has a single query.  An empty sequence gets o = 0
+ * and lse = -inf.
+ * Inputs  q_dev [num_seqs, Hq, d] bf16 (one new query per sequence),
+ *         k_dev / v_dev [T, Hkv, d] bf16 (the packed cache, T = total_tokens),
+ *         cu_seqlens_dev int32 [num_seqs + 1], modes_dev uint8 [num_seqs * Hkv]
+ *         (sanitised on the device as for the prefill).
+ * Outputs o_out_dev [num_seqs, Hq, d] bf16, lse_out_dev [num_seqs, Hq] fp32.
+ * The descriptor's block / xa fields must be valid but are unused; Hq / Hkv
+ * <= 16 (EA_ERR_UNSUPPORTED otherwise).
+ * Workspace: ea_workspace_bytes(desc, EA_OP_DECODE) bytes of device memory
+ * (fp32 partial results of the key splits).
+ */
+ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
+                                const void* v_dev, const int32_t* cu_seqlens_dev,
+                                const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
+                                void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * Attention Router, inference pass (English paper-reading notes, 03 Method,

@@ -277,3 +277,31 @@ def test_route_heads_rejects_bad_arguments():
     # No sequence: nothing to do, nothing touched.
     d = desc(num_seqs=0, total_tokens=0, max_seqlen=0)
     assert call(_router_desc(), modes=None, k=None) == E.EA_OK
+
+
+def test_decode_rejects_bad_arguments_and_sizes_workspace():
+    L = E.lib()
+    d = desc()
+    need = E.ea_workspace_bytes(d, E.EA_OP_DECODE)
+    # fp32 partials: num_seqs * Hq * ceil(max_seqlen / 1024) * (d + 2) floats, plus metadata
+    assert need >= 4 * 1 * 32 * 4 * 130
+
+    def call(dd=None, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, modes=FAKE, o=FAKE, lse=FAKE, ws=FAKE, n=need)
+        a.update(kw)
+        return L.ea_hybrid_attn_decode(ctypes.byref(dd or d), a["q"], a["k"], a["v"], a["cu"],
+                                       a["modes"], a["o"], a["lse"], a["ws"], a["n"], None)
+
+    bad = E.EA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "cu", "modes", "o", "lse"):
+        assert call(**{name: None}) == bad, name
+    for name in ("q", "k", "v", "o"):
+        assert call(**{name: FAKE + 2}) == bad, name
+    assert call(lse=FAKE + 2) == bad
+    assert call(ws=None) == E.EA_ERR_WORKSPACE
+    assert call(n=need - 1) == E.EA_ERR_WORKSPACE
+    assert call(desc(num_q_heads=34, num_kv_heads=2)) == E.EA_ERR_UNSUPPORTED   # G = 17
+    assert call(desc(head_dim=96)) == E.EA_ERR_UNSUPPORTED
+    empty = desc(num_seqs=0, total_tokens=0, max_seqlen=0)
+    assert call(empty, q=None, k=None, v=None, o=None, lse=None,
+                n=E.ea_workspace_bytes(empty, E.EA_OP_DECODE)) == E.EA_OK

@@ -12,7 +12,9 @@ Reported beside the throughput: ms per layer, tokens/s, effective TFLOP/s
 (4 B^2 d per computed tile) and pair-level TFLOP/s (4 d per attended pair),
 the speedup over the same kernel with every head in FA mode, the roofline of
 the attention kernel, the latency of the attention router (ea_route_heads,
-off the hot path) and the fp64 oracle timed on the host cores.
+off the hot path), one decode step over a batch of caches of the same
+length and modes (ea_hybrid_attn_decode, HBM-bound, with its own roofline)
+and the fp64 oracle timed on the host cores.
 """
 
 import argparse
@@ -39,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-fa", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--decode-batch", type=int, default=8,
+                    help="sequences of the decode measurement (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -228,6 +232,60 @@ def cpu_baseline(inp, seconds):
                        f"wall {time.perf_counter() - t0:.1f} s")
 
 
+def decode_bench(cfg, mode_row, L, batch, steps, warmup):
+    """One decode step over `batch` caches of length L with the workload's
+    head modes (`mode_row`, one per KV head).
+    The cache and queries are seeded N(0, 1) on the device (timing only; the
+    parity tests use the oracle's inputs).  Bytes are algorithmic: every kept
+    K and V row once, plus q and o."""
+    import torch
+    from hybrid_sparse_full_amd.layer import HybridDecode, make_desc
+    D, Hq, Hkv = cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
+    modes = np.repeat(np.asarray(mode_row, dtype=np.uint8).reshape(1, -1), batch, axis=0)
+    T = L * batch
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    k = torch.randn((T, Hkv, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((T, Hkv, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((batch, Hq, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    cu = np.arange(batch + 1, dtype=np.int32) * L
+    desc = make_desc(num_seqs=batch, total_tokens=T, max_seqlen=L, num_q_heads=Hq, num_kv_heads=Hkv,
+                     head_dim=D, block=cfg.block, softmax_scale=cfg.softmax_scale, ssa_sink=cfg.ssa_sink,
+                     ssa_window=cfg.ssa_window, xa_stride=cfg.xa_stride, xa_tau=(cfg.tau_num, cfg.tau_den))
+
+    def kept(mode):
+        if mode == 1:  # SSA: sink plus window of the decoded query
+            head = min(cfg.ssa_sink, L)
+            return head + max(0, L - max(head, L - cfg.ssa_window))
+        return L
+
+    def run(m):
+        dec = HybridDecode(desc, cu, m, device=dev)
+        _, ms, _ = time_steps(lambda: dec(q, k, v), steps, warmup)
+        keys = sum(kept(int(x)) for x in m.reshape(-1))
+        nbytes = keys * 2 * D * 2 + 2 * (batch * Hq * D * 2) + batch * Hq * 4
+        return ms, nbytes
+
+    ms, nbytes = run(modes)
+    fa_ms, fa_bytes = run(np.zeros_like(modes))
+    del k, v
+    torch.cuda.synchronize()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"{cfg.name} decode, {batch} sequences x {L} cached tokens",
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(batch / (ms * 1e-3), 1),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"kernel": "k_decode + k_decode_combine", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
+        "all_fa_ms_per_step": round(fa_ms, 5),
+        "all_fa_gbs": round(fa_bytes / (fa_ms * 1e-3) / 1e9, 1),
+        "speedup_vs_all_fa": round(fa_ms / ms, 4),
+        "data": "seeded N(0,1) cache on the device",
+    }
+
+
 def main():
     a = parse()
     if a.calibrate_copy:
@@ -286,6 +344,11 @@ def main():
     _, router_ms, _ = time_steps(lambda: router(desc, k, layer.cu, 0, cfg.sparse_mode, routed),
                                  max(a.steps, 20), a.warmup)
 
+    decode = None
+    if a.decode_batch > 0:
+        decode = decode_bench(cfg, inp["modes"][0], int(np.max(inp["seqlens"])), a.decode_batch,
+                              max(a.steps, 20), a.warmup)
+
     speedup = None
     allfa_ms = None
     if not a.no_all_fa:
@@ -333,6 +396,7 @@ def main():
         "omega_msr": round(float(rat["msr"][-1]), 6),
         "omega_esr": round(float(rat["esr"][-1]), 6),
         "omega_esr_pair_weighted": round(rat["esr_pairs"], 6),
+        "decode": decode,
         "router": {
             "ms": round(router_ms, 4),
             "heads_routed": desc.num_seqs * desc.num_kv_heads,

@@ -8,29 +8,31 @@
 // A decode step reads each kept K/V row once and does 4 d flops per key and
 // q-head, ~4 flop per byte: it is bound by HBM bandwidth, so it runs on the
 // vector ALU with bf16 dot products, not on the matrix core.  Design:
-//   * split-K: workgroup (split s, KV head g, sequence b) takes key-set
-//     positions [1024 s, 1024 s + 1024) of its head's kept keys (the key set
-//     is compressed: an SSA head's split 0 covers the sink and the start of
-//     the window), for all G q-heads of g, so each K/V row is read once;
-//   * 64 keys per step, one per lane: K rows and V rows of the next step are
-//     loaded into registers while the current one is computed, then stored
-//     to one of two LDS buffers.  K pieces (16 B) are XOR-swizzled within a
-//     row so that the per-lane row reads are free of bank conflicts; V rows
-//     are stored with consecutive key pairs interleaved per column, so that
-//     P V is one v_dot2_f32_bf16 per key pair and column;
-//   * scores: lane r computes c <q, k_r> with v_dot2_f32_bf16 (q read from
-//     LDS as a broadcast); exact online softmax per step in the exp2 domain;
-//     P is rounded to bf16 for the P V dot products (as in the prefill
-//     kernel) while the row sum stays in fp32;
-//   * each split writes (m, l, unnormalised o) in fp32; a second kernel
-//     combines the splits of every (sequence, q-head) and writes o (bf16) and
-//     lse (fp32).
+//   * split-K over waves: one wave takes a split of 256 to 4096 kept-key
+//     positions (sized from the descriptor) of one (sequence, KV head) for
+//     GW of its q-heads (all G when G <= 8), so each
+//     K/V row is read once per GW heads.  The key set is compressed: an SSA
+//     head's first split covers the sink and the start of the window.
+//     Waves are independent: no LDS staging and no workgroup barrier;
+//   * lane layout: a key row of d bf16 is spread over d / 8 lanes, 16 bytes
+//     each, so one wave load moves 64 / (d / 8) whole rows (contiguous 2 d
+//     bytes per row) of K and of V;
+//   * latency: K and V of three blocks of 4 iterations sit in a register
+//     ring, two blocks in flight while one is computed;
+//   * q . k: 4 v_dot2_f32_bf16 per lane and head, then a sum over the row's
+//     lanes with DPP (quad swaps and row mirrors); exact online softmax per
+//     block in the exp2 domain; P is rounded to bf16 and P V uses one
+//     v_dot2_f32_bf16 per pair of iterations and column (the pairs built
+//     with v_perm_b32), while the row sum stays in fp32;
+//   * each wave writes (m, l, unnormalised o) of its split in fp32; a second
+//     kernel combines the splits of every (sequence, q-head) into o (bf16)
+//     and lse (fp32).
 #include "ea_device.h"
 
 namespace ea {
 
-constexpr int DEC_NT = 256;       // 4 waves
-constexpr int DEC_KEYS = 64;      // keys per step (one per lane)
+constexpr int DEC_BI = 4;   // iterations per softmax block
+constexpr int DEC_NB = 3;   // blocks in the register ring
 
 struct DecArgs {
   const uint16_t* q;   // [nseq, Hq, D]
@@ -39,7 +41,7 @@ struct DecArgs {
   const int32_t* cu;
   const uint8_t* modes;
   float* part;         // [nseq, Hq, nsplit_max, D + 2]
-  int32_t nseq, Hq, Hkv, G, T, maxL, sink, window, nsplit_max;
+  int32_t nseq, Hq, Hkv, G, T, maxL, sink, window, split, nsplit_max;
   float c2;            // softmax scale * log2(e)
 };
 
@@ -65,208 +67,230 @@ __device__ inline void seq_bounds(const DecArgs& a, int b, int32_t* s0, int32_t*
   *L = e - s;
 }
 
-template <int D, int HPW>
-__global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
-  constexpr int NP = D / 8;                     // 16-byte pieces per row
-  constexpr int KPIECES = DEC_KEYS * NP;        // K pieces per step
-  constexpr int VUNITS = (DEC_KEYS / 2) * NP;   // V (key pair, piece) units per step
-  constexpr int KPT = KPIECES / DEC_NT;         // per thread
-  constexpr int VPT = VUNITS / DEC_NT;
-  constexpr int CPL = D / 64;                   // output columns per lane
-  static_assert(KPT >= 1 && VPT >= 1, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][DEC_KEYS * D];
-  __shared__ __attribute__((aligned(16))) uint32_t vs[2][(DEC_KEYS / 2) * D];
-  __shared__ __attribute__((aligned(16))) uint16_t qs[16 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[4][DEC_KEYS];
+// Sum over the LPK lanes that hold one key row (LPK = 8 or 16, aligned).
+template <int LPK>
+__device__ inline float row_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // lane ^ 1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // lane ^ 2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false)); // half-row mirror
+  if (LPK == 16)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));  // row mirror
+  return x;
+}
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+// Max / sum over the key groups of the wave (lanes LPK, 2 LPK, ... apart).
+template <int LPK>
+__device__ inline float groups_max(float x) {
+  if (LPK == 8)
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));  // row_ror:8
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return halves_max(x);
+}
+template <int LPK>
+__device__ inline float groups_sum(float x) {
+  if (LPK == 8)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  return halves_sum(x);
+}
+
+template <int D, int GW>
+__global__ __launch_bounds__(256) void k_decode(DecArgs a) {
+  constexpr int LPK = D / 8;          // lanes per key row
+  constexpr int KPI = 64 / LPK;       // keys per wave iteration
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / LPK, pc = lane % LPK;
+  // Wave -> (split, head group, KV head, sequence); split fastest.
+  const int nwg = a.G / GW;
+  int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int split = (int)(w % a.nsplit_max);
+  w /= a.nsplit_max;
+  const int wg = (int)(w % nwg);
+  w /= nwg;
+  const int g = (int)(w % a.Hkv);
+  const int b = (int)(w / a.Hkv);
+  if (b >= a.nseq) return;
   int32_t s0, L;
   seq_bounds(a, b, &s0, &L);
   int mode = sane_mode(a.modes[(size_t)b * a.Hkv + g]);
   if (mode == EA_MODE_XA) mode = EA_MODE_FA;
   const int32_t n = dec_kept(mode, L, a.sink, a.window);
-  const int32_t p0 = s * DEC_SPLIT;
-  if (p0 >= n) return;  // uniform over the workgroup
-  const int32_t p1 = min(n, p0 + DEC_SPLIT);
-  const int nsteps = (p1 - p0 + DEC_KEYS - 1) / DEC_KEYS;
+  const int32_t p0 = split * a.split;
+  if (p0 >= n) return;  // wave-uniform
+  const int32_t p1 = min(n, p0 + a.split);
+  const int nit = (p1 - p0 + KPI - 1) / KPI;
+  const int nblk = (nit + DEC_BI - 1) / DEC_BI;
+  const int h0 = g * a.G + wg * GW;
 
-  // q of the group's G heads into LDS (bf16).
-  for (int i = tid; i < a.G * NP; i += DEC_NT) {
-    const int hh = i / NP, c = i % NP;
-    *(uint4*)(qs + hh * D + c * 8) =
-        *(const uint4*)(a.q + ((size_t)b * a.Hq + g * a.G + hh) * D + c * 8);
+  // This lane's 16-byte piece of each of the GW queries.
+  uint32_t qw[GW][4];
+#pragma unroll
+  for (int hh = 0; hh < GW; ++hh) {
+    const uint4 t = *(const uint4*)(a.q + ((size_t)b * a.Hq + h0 + hh) * D + 8 * pc);
+    qw[hh][0] = t.x; qw[hh][1] = t.y; qw[hh][2] = t.z; qw[hh][3] = t.w;
   }
 
-  // Global -> registers for step t.
-  uint4 kr[KPT], vr[VPT][2];
-  auto load_step = [&](int t) {
-    const int32_t base = p0 + t * DEC_KEYS;
+  uint4 kr[DEC_NB][DEC_BI], vr[DEC_NB][DEC_BI];
+  auto load_block = [&](int blk, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + i * DEC_NT;
-      const int r = idx / NP, c = idx % NP;
-      const int32_t p = min(base + r, p1 - 1);
+    for (int i = 0; i < DEC_BI; ++i) {
+      const int32_t p = min(p0 + (blk * DEC_BI + i) * KPI + grp, p1 - 1);
       const int32_t j = dec_key(mode, p, L, a.sink, a.window);
-      kr[i] = *(const uint4*)(a.k + ((size_t)(s0 + j) * a.Hkv + g) * D + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + i * DEC_NT;
-      const int rp = idx / NP, c = idx % NP;
-      const int32_t pa = min(base + 2 * rp, p1 - 1), pb = min(base + 2 * rp + 1, p1 - 1);
-      const int32_t ja = dec_key(mode, pa, L, a.sink, a.window);
-      const int32_t jb = dec_key(mode, pb, L, a.sink, a.window);
-      vr[i][0] = *(const uint4*)(a.v + ((size_t)(s0 + ja) * a.Hkv + g) * D + c * 8);
-      vr[i][1] = *(const uint4*)(a.v + ((size_t)(s0 + jb) * a.Hkv + g) * D + c * 8);
-    }
-  };
-  // Registers -> LDS buffer `buf`: K piece c of row r at physical piece
-  // c ^ (r mod NP); V as key pairs interleaved per column: word (rp, col)
-  // holds (v[2 rp][col], v[2 rp + 1][col]).
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + i * DEC_NT;
-      const int r = idx / NP, c = idx % NP;
-      *(uint4*)(ks[buf] + r * D + ((c ^ (r & (NP - 1))) * 8)) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + i * DEC_NT;
-      const int rp = idx / NP, c = idx % NP;
-      const uint32_t* x = (const uint32_t*)&vr[i][0];
-      const uint32_t* y = (const uint32_t*)&vr[i][1];
-      uint4 w0, w1;
-      // low half of each word = key 2 rp, high half = key 2 rp + 1
-      w0.x = __builtin_amdgcn_perm(y[0], x[0], 0x05040100u);
-      w0.y = __builtin_amdgcn_perm(y[0], x[0], 0x07060302u);
-      w0.z = __builtin_amdgcn_perm(y[1], x[1], 0x05040100u);
-      w0.w = __builtin_amdgcn_perm(y[1], x[1], 0x07060302u);
-      w1.x = __builtin_amdgcn_perm(y[2], x[2], 0x05040100u);
-      w1.y = __builtin_amdgcn_perm(y[2], x[2], 0x07060302u);
-      w1.z = __builtin_amdgcn_perm(y[3], x[3], 0x05040100u);
-      w1.w = __builtin_amdgcn_perm(y[3], x[3], 0x07060302u);
-      uint32_t* dst = vs[buf] + rp * D + c * 8;
-      *(uint4*)dst = w0;
-      *(uint4*)(dst + 4) = w1;
+      const size_t off = ((size_t)(s0 + j) * a.Hkv + g) * D + 8 * pc;
+      kr[sl][i] = *(const uint4*)(a.k + off);
+      vr[sl][i] = *(const uint4*)(a.v + off);
     }
   };
 
-  // Per-head state: this wave owns heads wv, wv + 4, ... < G (HPW of them).
-  float m[HPW], l[HPW], o[HPW][CPL];
+  float m[GW], l[GW], o[GW][8];
 #pragma unroll
-  for (int u = 0; u < HPW; ++u) {
-    m[u] = -INFINITY;
-    l[u] = 0.f;
+  for (int hh = 0; hh < GW; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) o[u][c] = 0.f;
+    for (int c = 0; c < 8; ++c) o[hh][c] = 0.f;
   }
 
-  load_step(0);
-  for (int t = 0; t < nsteps; ++t) {
-    const int buf = t & 1;
-    store_step(buf);
-    __syncthreads();
-    if (t + 1 < nsteps) load_step(t + 1);
-    const bool valid = p0 + t * DEC_KEYS + lane < p1;
-    const uint16_t* krow = ks[buf] + lane * D;
+  auto compute_block = [&](int blk, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    bool valid[DEC_BI];
 #pragma unroll
-    for (int u = 0; u < HPW; ++u) {
-      const int hh = wv + 4 * u;
-      if (hh >= a.G) break;  // wave-uniform
-      // Score of key `lane`.
-      float acc = 0.f;
-      const uint16_t* qh = qs + hh * D;
+    for (int i = 0; i < DEC_BI; ++i) valid[i] = p0 + (blk * DEC_BI + i) * KPI + grp < p1;
+    // V of iteration pairs as (v_i[col], v_{i+1}[col]) words.
+    uint32_t vp[DEC_BI / 2][8];
 #pragma unroll
-      for (int c = 0; c < NP; ++c) {
-        const uint4 kk = *(const uint4*)(krow + ((c ^ (lane & (NP - 1))) * 8));
-        const uint4 qq = *(const uint4*)(qh + c * 8);
-        const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w}, qw[4] = {qq.x, qq.y, qq.z, qq.w};
+    for (int i = 0; i < DEC_BI; i += 2) {
+      const uint32_t x[4] = {vr[sl][i].x, vr[sl][i].y, vr[sl][i].z, vr[sl][i].w};
+      const uint32_t y[4] = {vr[sl][i + 1].x, vr[sl][i + 1].y, vr[sl][i + 1].z, vr[sl][i + 1].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vp[i / 2][2 * e] = __builtin_amdgcn_perm(y[e], x[e], 0x05040100u);
+        vp[i / 2][2 * e + 1] = __builtin_amdgcn_perm(y[e], x[e], 0x07060302u);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) {
+      float x[DEC_BI];
+#pragma unroll
+      for (int i = 0; i < DEC_BI; ++i) {
+        const uint32_t kw[4] = {kr[sl][i].x, kr[sl][i].y, kr[sl][i].z, kr[sl][i].w};
+        float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]),
-                                               __builtin_bit_cast(bf16x2, qw[e]), acc, false);
+                                               __builtin_bit_cast(bf16x2, qw[hh][e]), acc, false);
+        acc = row_sum<LPK>(acc);
+        x[i] = valid[i] ? acc * a.c2 : -INFINITY;
       }
-      const float x = valid ? acc * a.c2 : -INFINITY;
-      const float mn = fmaxf(m[u], wave_max(x));
-      const float alpha = __builtin_amdgcn_exp2f(m[u] - mn);  // m = -inf at the start: 0
-      const float p = __builtin_amdgcn_exp2f(x - mn);
-      l[u] = l[u] * alpha + wave_sum(p);
-      m[u] = mn;
-      // P in bf16 pairs through LDS (this wave's own slice).
-      pbuf[wv][lane] = __builtin_bit_cast(uint16_t, (__bf16)p);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const uint32_t* pp = (const uint32_t*)pbuf[wv];
+      float bm = x[0];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) o[u][c] *= alpha;
+      for (int i = 1; i < DEC_BI; ++i) bm = fmaxf(bm, x[i]);
+      const float mn = fmaxf(m[hh], groups_max<LPK>(bm));
+      const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);  // m = -inf at the start: 0
+      m[hh] = mn;
+      float pf[DEC_BI], ps = 0.f;
 #pragma unroll
-      for (int rp4 = 0; rp4 < DEC_KEYS / 2; rp4 += 4) {
-        const uint4 p4 = *(const uint4*)(pp + rp4);
-        const uint32_t pw[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t* vrow = vs[buf] + (rp4 + e) * D + CPL * lane;
-          const bf16x2 pv = __builtin_bit_cast(bf16x2, pw[e]);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            o[u][c] = __builtin_amdgcn_fdot2_f32_bf16(pv, __builtin_bit_cast(bf16x2, vrow[c]), o[u][c], false);
-        }
+      for (int i = 0; i < DEC_BI; ++i) {
+        pf[i] = __builtin_amdgcn_exp2f(x[i] - mn);
+        ps += pf[i];
       }
-      // The next head's P overwrites pbuf after these reads.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      l[hh] = l[hh] * alpha + ps;  // this key group's keys; groups are summed at the end
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[hh][c] *= alpha;
+#pragma unroll
+      for (int i = 0; i < DEC_BI; i += 2) {
+        const bf16x2 pp = {(__bf16)pf[i], (__bf16)pf[i + 1]};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          o[hh][c] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vp[i / 2][c]), o[hh][c],
+                                                     false);
+      }
     }
+  };
+
+  // Block blk lives in ring slot blk % 3; the body is unrolled three times so
+  // that slots are compile-time register sets.
+  load_block(0, std::integral_constant<int, 0>());
+  if (nblk > 1) load_block(1, std::integral_constant<int, 1>());
+  auto body = [&](int blk, auto slot_c, auto next_c) {
+    if (blk + 2 < nblk) load_block(blk + 2, next_c);
+    compute_block(blk, slot_c);
+  };
+  for (int blk = 0; blk < nblk; blk += DEC_NB) {
+    body(blk, std::integral_constant<int, 0>(), std::integral_constant<int, 2>());
+    if (blk + 1 < nblk) body(blk + 1, std::integral_constant<int, 1>(), std::integral_constant<int, 0>());
+    if (blk + 2 < nblk) body(blk + 2, std::integral_constant<int, 2>(), std::integral_constant<int, 1>());
   }
 
-  // Partial results of this split.
+  // Sum the key groups (m is already wave-uniform) and write the split.
 #pragma unroll
-  for (int u = 0; u < HPW; ++u) {
-    const int hh = wv + 4 * u;
-    if (hh >= a.G) break;
-    float* dst = a.part + (((size_t)b * a.Hq + g * a.G + hh) * a.nsplit_max + s) * (D + 2);
+  for (int hh = 0; hh < GW; ++hh) {
+    const float lt = groups_sum<LPK>(l[hh]);
+    float* dst = a.part + (((size_t)b * a.Hq + h0 + hh) * a.nsplit_max + split) * (D + 2);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) dst[CPL * lane + c] = o[u][c];
+    for (int c = 0; c < 8; ++c) {
+      const float oc = groups_sum<LPK>(o[hh][c]);
+      if (grp == 0) dst[8 * pc + c] = oc;
+    }
     if (lane == 0) {
-      dst[D] = m[u];
-      dst[D + 1] = l[u];
+      dst[D] = m[hh];
+      dst[D + 1] = lt;
     }
   }
 }
 
-// Combine the splits of one (sequence, q-head): 64 threads, CPL columns each.
+// Combine the splits of one (sequence, q-head).  256 threads: the split
+// maxima are reduced over the workgroup; then wave w folds splits w, w + 4,
+// ... (lanes own CPL columns, loads of several splits in flight) and the
+// four waves meet in LDS.
 template <int D>
-__global__ __launch_bounds__(64) void k_decode_combine(DecArgs a, uint16_t* out, float* lse) {
+__global__ __launch_bounds__(256) void k_decode_combine(DecArgs a, uint16_t* out, float* lse) {
   constexpr int CPL = D / 64;
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  __shared__ float red[4 * (D + 2)];
+  __shared__ float mred[4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   int32_t s0, L;
   seq_bounds(a, b, &s0, &L);
   int mode = sane_mode(a.modes[(size_t)b * a.Hkv + h / a.G]);
   if (mode == EA_MODE_XA) mode = EA_MODE_FA;
   const int32_t n = dec_kept(mode, L, a.sink, a.window);
-  const int ns = (n + DEC_SPLIT - 1) / DEC_SPLIT;
+  const int ns = (n + a.split - 1) / a.split;
   const float* src = a.part + ((size_t)b * a.Hq + h) * a.nsplit_max * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, src[s * (D + 2) + D]);
+  for (int s = tid; s < ns; s += 256) M = fmaxf(M, src[(size_t)s * (D + 2) + D]);
+  M = wave_max(M);
+  if (lane == 0) mred[wv] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
   float Ls = 0.f, acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __builtin_amdgcn_exp2f(src[s * (D + 2) + D] - M);
-    Ls += w * src[s * (D + 2) + D + 1];
+#pragma unroll 4
+  for (int s = wv; s < ns; s += 4) {
+    const float* row = src + (size_t)s * (D + 2);
+    const float w = __builtin_amdgcn_exp2f(row[D] - M);
+    Ls += w * row[D + 1];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] += w * src[s * (D + 2) + CPL * lane + c];
+    for (int c = 0; c < CPL; ++c) acc[c] += w * row[CPL * lane + c];
   }
-  uint16_t* orow = out + ((size_t)b * a.Hq + h) * D;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const float val = ns > 0 ? acc[c] / Ls : 0.f;
-    orow[CPL * lane + c] = __builtin_bit_cast(uint16_t, (__bf16)val);
+  for (int c = 0; c < CPL; ++c) red[wv * (D + 2) + CPL * lane + c] = acc[c];
+  if (lane == 0) red[wv * (D + 2) + D] = Ls;
+  __syncthreads();
+  if (wv == 0) {
+    const float Lt = red[D] + red[(D + 2) + D] + red[2 * (D + 2) + D] + red[3 * (D + 2) + D];
+    uint16_t* orow = out + ((size_t)b * a.Hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int col = CPL * lane + c;
+      const float v = red[col] + red[(D + 2) + col] + red[2 * (D + 2) + col] + red[3 * (D + 2) + col];
+      orow[col] = __builtin_bit_cast(uint16_t, (__bf16)(ns > 0 ? v / Lt : 0.f));
+    }
+    if (lane == 0) lse[(size_t)b * a.Hq + h] = ns > 0 ? (M + __log2f(Lt)) * LN2 : -INFINITY;
   }
-  if (lane == 0) lse[(size_t)b * a.Hq + h] = ns > 0 ? (M + __log2f(Ls)) * LN2 : -INFINITY;
 }
 
 hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -287,19 +311,23 @@ hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, 
   a.maxL = d.maxL;
   a.sink = d.sink;
   a.window = d.window;
+  a.split = decode_split(d);
   a.nsplit_max = decode_splits(d);
   a.c2 = d.scale * LOG2E;
   if (a.nsplit_max > 0) {
-    const dim3 grid((unsigned)a.nsplit_max, (unsigned)d.Hkv, (unsigned)d.nseq);
-    const int hpw = (d.G + 3) / 4;  // q-heads per wave: 1, 2, 3 or 4
+    const int gw = decode_gw(d);
+    const int64_t waves = (int64_t)d.nseq * d.Hkv * (d.G / gw) * a.nsplit_max;
+    const dim3 grid((unsigned)((waves + 3) / 4));
     void (*kern)(DecArgs) = nullptr;
-    if (d.D == 128) kern = hpw == 1 ? k_decode<128, 1> : hpw == 2 ? k_decode<128, 2> : k_decode<128, 4>;
-    else kern = hpw == 1 ? k_decode<64, 1> : hpw == 2 ? k_decode<64, 2> : k_decode<64, 4>;
-    hipLaunchKernelGGL(kern, grid, dim3(DEC_NT), 0, st, a);
+    if (d.D == 128)
+      kern = gw == 8 ? k_decode<128, 8> : gw == 4 ? k_decode<128, 4> : gw == 2 ? k_decode<128, 2> : k_decode<128, 1>;
+    else
+      kern = gw == 8 ? k_decode<64, 8> : gw == 4 ? k_decode<64, 4> : gw == 2 ? k_decode<64, 2> : k_decode<64, 1>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
   }
   const dim3 cgrid((unsigned)d.Hq, (unsigned)d.nseq);
-  if (d.D == 128) hipLaunchKernelGGL(k_decode_combine<128>, cgrid, dim3(64), 0, st, a, o, lse);
-  else hipLaunchKernelGGL(k_decode_combine<64>, cgrid, dim3(64), 0, st, a, o, lse);
+  if (d.D == 128) hipLaunchKernelGGL(k_decode_combine<128>, cgrid, dim3(256), 0, st, a, o, lse);
+  else hipLaunchKernelGGL(k_decode_combine<64>, cgrid, dim3(256), 0, st, a, o, lse);
   return hipGetLastError();
 }
 

@@ -78,9 +78,20 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v
                            const WsLayout& L, hipStream_t st);
 hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint8_t* modes, const SeqMeta& m, void* ws,
                             const WsLayout& L, uint16_t* o, float* lse, hipStream_t st);
-// Decode: key-set positions per split workgroup, and the split bound.
-constexpr int32_t DEC_SPLIT = 1024;
-inline int32_t decode_splits(const EaDims& d) { return (d.maxL + DEC_SPLIT - 1) / DEC_SPLIT; }
+// Decode: kept-key positions per split (one wave each), chosen from the
+// descriptor alone so that an all-FA step would spread over about 2048
+// waves (8 per CU): a power of two in [256, 4096].  Longer splits amortise a
+// wave's pipeline start; more splits fill the chip when the batch is small.
+inline int32_t decode_gw(const EaDims& d) {
+  return d.G % 8 == 0 ? 8 : d.G % 4 == 0 ? 4 : d.G % 2 == 0 ? 2 : 1;
+}
+inline int32_t decode_split(const EaDims& d) {
+  const int64_t work = (int64_t)d.T * d.Hkv * (d.G / decode_gw(d));
+  int32_t s = 256;
+  while (s < 4096 && (int64_t)s * 2048 < work) s *= 2;
+  return s;
+}
+inline int32_t decode_splits(const EaDims& d) { return (d.maxL + decode_split(d) - 1) / decode_split(d); }
 hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* cu, const uint8_t* modes, void* ws, uint16_t* o, float* lse,
                          hipStream_t st);

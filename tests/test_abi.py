@@ -283,8 +283,9 @@ def test_decode_rejects_bad_arguments_and_sizes_workspace():
     L = E.lib()
     d = desc()
     need = E.ea_workspace_bytes(d, E.EA_OP_DECODE)
-    # fp32 partials: num_seqs * Hq * ceil(max_seqlen / 1024) * (d + 2) floats, plus metadata
-    assert need >= 4 * 1 * 32 * 4 * 130
+    # fp32 partials: num_seqs * Hq * ceil(max_seqlen / split) * (d + 2) floats, plus
+    # metadata; 4096 tokens x 8 KV heads / 2048 waves -> split 256, 16 splits
+    assert need >= 4 * 1 * 32 * 16 * 130
 
     def call(dd=None, **kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, modes=FAKE, o=FAKE, lse=FAKE, ws=FAKE, n=need)

@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--decode-batch", type=int, default=8,
                     help="sequences of the decode measurement (0 skips it)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="measure only the decode step (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -303,6 +305,14 @@ def main():
     from synth import get_config, make_inputs
 
     cfg = get_config(a.config)
+    if a.decode_only:
+        meta = make_inputs(cfg, with_values=False)
+        torch.cuda.set_device(0)
+        r = decode_bench(cfg, meta["modes"][0], int(np.max(meta["seqlens"])), max(a.decode_batch, 1),
+                         max(a.steps, 20), a.warmup)
+        print(json.dumps({"metric": "decode step HBM GB/s (kept K/V, q, o)", "value": r["roofline"]["achieved"],
+                          "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "decode": r}), flush=True)
+        return
     inp = make_inputs(cfg)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

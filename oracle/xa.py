@@ -31,7 +31,8 @@ Selection (integer-exact)
 
 Parity status: the scoring normalization (R2), the reduced-level causal rule,
 the scale c on every product, the union rule for forced blocks and the
-tie-break are readings, not fixed by the pages; they are pinned only by
+tie-break are readings, not fixed by the pages (as is the optional
+one-mask-per-KV-head variant, group_query); they are pinned only by
 self-consistency (q = 0 closed form, brute-force antidiagonal enumeration,
 row normalization, subset brute force of the selector) -- parity unpinned by
 the pages themselves.
@@ -160,6 +161,14 @@ def kept_pairs(mask, L, B):
             else:
                 total += B * (B + 1) // 2
     return total
+
+
+def group_query(q_group):
+    """Reading S9-group: one XA mask per KV head.  The antidiagonal scores are
+    linear in the query, so the mean of the group's per-head scores s^_h is
+    the score of the group-mean query; P, the weights and the selection then
+    follow the per-head steps unchanged.  q_group [G, L, d] -> [L, d]."""
+    return np.asarray(q_group, dtype=np.float64).mean(axis=0)
 
 
 def head_mask(qh, kg, S, B, scale, tau_num, tau_den, rows=None):

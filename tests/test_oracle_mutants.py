@@ -180,3 +180,9 @@ def test_mutant_decode_query_one_back(monkeypatch):
     monkeypatch.setattr(OD, "row_attention", one_back)
     with pytest.raises(AssertionError):
         TD.test_zero_query_closed_form(13, 4, 8)
+
+
+def test_mutant_group_scores_summed(monkeypatch):
+    monkeypatch.setattr(OX, "group_query", lambda q: np.asarray(q, dtype=np.float64).sum(axis=0))  # planted
+    with pytest.raises(AssertionError):
+        TX.test_group_query_is_the_mean_of_the_scores()

@@ -162,3 +162,25 @@ def test_r1_normalization_is_nearly_one_hot():
     P2 = OX.block_mass(q, k, S, B, d ** -0.5, rows=[7])
     assert P1[7, :8].max() > 0.99
     assert P2[7, :8].max() < 0.5
+
+
+def test_group_query_is_the_mean_of_the_scores():
+    # The group mask is scored with the mean query: its reduced scores are the
+    # mean of the heads' reduced scores (brute force), not their sum, and a
+    # group of identical heads selects exactly the per-head mask.
+    rng = np.random.default_rng(9)
+    L, d, S, B, G = 64, 8, 4, 16, 4
+    qg = rng.standard_normal((G, L, d))
+    kg = rng.standard_normal((L, d))
+    qm = OX.group_query(qg)
+    n = L // S
+    for a in range(n):
+        for bq in range(a + 1):
+            per_head = [sum(qg[h, a * S + t] @ kg[bq * S + S - 1 - t] for t in range(S)) for h in range(G)]
+            pooled = sum(qm[a * S + t] @ kg[bq * S + S - 1 - t] for t in range(S))
+            assert np.isclose(pooled, np.mean(per_head), rtol=1e-12, atol=1e-12)
+    same = np.repeat(qg[:1], G, axis=0)
+    m1, P1 = OX.head_mask(qg[0], kg, S, B, 0.3, 9, 10)
+    mg, Pg = OX.head_mask(OX.group_query(same), kg, S, B, 0.3, 9, 10)
+    assert np.array_equal(m1, mg) and np.allclose(P1, Pg, rtol=1e-13, equal_nan=True)
+    assert np.array_equal(OX.group_query(qg[:1]), qg[0])

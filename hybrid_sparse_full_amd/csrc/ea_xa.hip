@@ -26,10 +26,13 @@ __device__ inline int64_t tri_root(int64_t loc) {
 
 // One scoring item is a 128 x 128 tile (reduced keys b' x reduced queries a)
 // of a group of HPI q-heads that share one KV head: the K~ chunk of every
-// stage is staged once and serves all HPI heads.  A stage is KC = 64 elements
+// stage is staged once and serves all HPI heads.  With GROUP (one mask per
+// KV head, HPI == G) the 8 waves split one tile and each accumulates the
+// products of all HPI heads into the same registers: the sum of the heads'
+// scores, divided by HPI in the epilogue, is the group-mean score.  A stage is KC = 64 elements
 // of the S * d reduction (one key row t of the antidiagonal, 64 of d); rows
 // of a staged tile are 128 bytes, 16-byte chunks XOR-swizzled by row % 8.
-template <int D, int R, int HPI>
+template <int D, int R, int HPI, bool GROUP = false>
 struct XaCfg {
   static constexpr int NW = 8;                   // waves per workgroup
   static constexpr int NT = NW * 64;
@@ -39,8 +42,9 @@ struct XaCfg {
   static constexpr int STAGE = (1 + HPI) * OPB;  // K~ then HPI Q~ tiles
   static constexpr int NS = HPI == 4 ? 2 : 3;    // stages in the LDS ring
   static constexpr int NI = STAGE / 1024 / NW;   // 1 KB DMA regions per wave per stage
-  static constexpr int WPH = NW / HPI;           // waves per head
-  static constexpr int AW = HPI == 1 ? 4 : WPH;  // waves along a (queries)
+  static constexpr int WPH = GROUP ? NW : NW / HPI;            // waves per output tile
+  static constexpr int AW = (GROUP || HPI == 1) ? 4 : WPH;     // waves along a (queries)
+  static constexpr int NHQ = GROUP ? HPI : 1;                  // heads summed by a wave
   static constexpr int BW = WPH / AW;            // waves along b' (keys)
   static constexpr int NA = XT / AW / 32;        // 32-query MFMA tiles per wave
   static constexpr int NB = XT / BW / 32;        // 32-key MFMA tiles per wave
@@ -48,23 +52,23 @@ struct XaCfg {
   static_assert((STAGE / 1024) % NW == 0, "DMA regions must split evenly over waves");
 };
 
-template <int D, int R, int HPI>
+template <int D, int R, int HPI, bool GROUP>
 __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __restrict__ q,
                                                   const uint16_t* __restrict__ k, SeqMeta m,
                                                   const int32_t* __restrict__ pair_bg,
                                                   const int64_t* __restrict__ pair_items,
                                                   float* __restrict__ lse_ws) {
-  using C = XaCfg<D, R, HPI>;
+  using C = XaCfg<D, R, HPI, GROUP>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int hh = wv / C::WPH;                      // head of the group
+  const int hh = GROUP ? 0 : wv / C::WPH;          // head of the group (GROUP: all)
   const int wa = (wv % C::WPH) % C::AW, wb = (wv % C::WPH) / C::AW;
   const int npairs = m.scal[SCAL_XA_PAIRS];
   const int64_t total = pair_items[npairs];
   unsigned long long* ctr = (unsigned long long*)(m.scal + SCAL_CTR64);
-  const float C2 = d.scale * LOG2E;
+  const float C2 = d.scale * LOG2E * (GROUP ? 1.0f / HPI : 1.0f);
   const int S = d.S;
   const int nhg = d.Hq / HPI;
   const int nst = S * D / C::KC;
@@ -158,25 +162,33 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
       const uint8_t* Ks = smem + slot + (size_t)wb * (C::NB * 32) * C::ROWB;
       const uint8_t* Qs = smem + slot + (size_t)(1 + hh) * C::OPB + (size_t)wa * (C::NA * 32) * C::ROWB;
       auto kf = [&](int j, int s) { return *(const bf16x8*)(Ks + (fa ^ (uint32_t)(s << 5)) + j * 32 * C::ROWB); };
-      auto qf = [&](int i, int s) { return *(const bf16x8*)(Qs + (fa ^ (uint32_t)(s << 5)) + i * 32 * C::ROWB); };
-      bf16x8 fk[2][C::NB], fq[2][C::NA];
+      auto qf = [&](int u, int i, int s) {
+        return *(const bf16x8*)(Qs + (size_t)u * C::OPB + (fa ^ (uint32_t)(s << 5)) + i * 32 * C::ROWB);
+      };
+      bf16x8 fk[2][C::NB], fq[2][C::NHQ][C::NA];
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) fk[0][j] = kf(j, 0);
 #pragma unroll
-      for (int i = 0; i < C::NA; ++i) fq[0][i] = qf(i, 0);
+      for (int u = 0; u < C::NHQ; ++u)
+#pragma unroll
+        for (int i = 0; i < C::NA; ++i) fq[0][u][i] = qf(u, i, 0);
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         if (s + 1 < C::KSTEPS) {
 #pragma unroll
           for (int j = 0; j < C::NB; ++j) fk[(s + 1) & 1][j] = kf(j, s + 1);
 #pragma unroll
-          for (int i = 0; i < C::NA; ++i) fq[(s + 1) & 1][i] = qf(i, s + 1);
+          for (int u = 0; u < C::NHQ; ++u)
+#pragma unroll
+            for (int i = 0; i < C::NA; ++i) fq[(s + 1) & 1][u][i] = qf(u, i, s + 1);
         }
 #pragma unroll
-        for (int i = 0; i < C::NA; ++i)
+        for (int u = 0; u < C::NHQ; ++u)
 #pragma unroll
-          for (int j = 0; j < C::NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[s & 1][j], fq[s & 1][i], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < C::NA; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[s & 1][j], fq[s & 1][u][i], acc[i][j], 0, 0, 0);
       }
     }
 
@@ -283,8 +295,11 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
   }
 
   const int64_t nqb = len / d.B;
+  // One mask per KV head: every q-head of the group reads the scores that the
+  // group's first head slot holds.
+  const int hs = d.xa_group ? h - h % d.G : h;
   const float* base =
-      lse_ws + (int64_t)R * (m.tri_prefix[b] * d.Hq + (int64_t)h * tri64(nqb)) + (int64_t)R * tri64(I);
+      lse_ws + (int64_t)R * (m.tri_prefix[b] * d.Hq + (int64_t)hs * tri64(nqb)) + (int64_t)R * tri64(I);
   // 1. Per reduced row a: La = log2 sum_J exp2(lse2[a, J]), one online pass
   //    (lane-local running max and sum, then merged over the wave).
   float La[R];
@@ -422,14 +437,19 @@ hipError_t launch_xa_score(const EaDims& d, const uint16_t* q, const uint16_t* k
   const int64_t* pair_items = (const int64_t*)(w + L.xa_pair_items);
   float* lse = (float*)(w + L.xa_lse);
   const dim3 grid((unsigned)device_cus());
-#define EA_SCORE(DD, RR, HH)                                                          \
-  hipLaunchKernelGGL((k_xa_score<DD, RR, HH>), grid, dim3(XaCfg<DD, RR, HH>::NT), 0, st, d, q, \
-                     k, m, pair_bg, pair_items, lse)
-#define EA_SCORE_H(DD, RR)                       \
-  do {                                           \
-    if (d.xa_hpi == 4) EA_SCORE(DD, RR, 4);      \
-    else if (d.xa_hpi == 2) EA_SCORE(DD, RR, 2); \
-    else EA_SCORE(DD, RR, 1);                    \
+#define EA_SCORE(DD, RR, HH, GG)                                                         \
+  hipLaunchKernelGGL((k_xa_score<DD, RR, HH, GG>), grid, dim3(XaCfg<DD, RR, HH, GG>::NT), 0, st, d, \
+                     q, k, m, pair_bg, pair_items, lse)
+#define EA_SCORE_G(DD, RR, HH)                                  \
+  do {                                                          \
+    if (d.xa_group && (HH) > 1) EA_SCORE(DD, RR, HH, true);     \
+    else EA_SCORE(DD, RR, HH, false);                           \
+  } while (0)
+#define EA_SCORE_H(DD, RR)                          \
+  do {                                              \
+    if (d.xa_hpi == 4) EA_SCORE_G(DD, RR, 4);       \
+    else if (d.xa_hpi == 2) EA_SCORE_G(DD, RR, 2);  \
+    else EA_SCORE_G(DD, RR, 1);                     \
   } while (0)
   if (d.D == 128) {
     if (d.r == 4) EA_SCORE_H(128, 4);
@@ -443,6 +463,7 @@ hipError_t launch_xa_score(const EaDims& d, const uint16_t* q, const uint16_t* k
     else EA_SCORE_H(64, 32);
   }
 #undef EA_SCORE_H
+#undef EA_SCORE_G
 #undef EA_SCORE
   return hipGetLastError();
 }

@@ -69,6 +69,9 @@ typedef struct {
   int32_t xa_stride;     /* S: divides B with B/S in {4, 8, 16, 32} */
   int32_t xa_tau_num;    /* tau = num/den, 0 < tau <= 1, den <= 2^20 */
   int32_t xa_tau_den;
+  int32_t xa_group;      /* 0: one XA mask per q-head; 1: one per KV head, scored
+                            with the mean of its q-heads' antidiagonal scores
+                            (needs Hq / Hkv in {1, 2, 4}) */
 } ea_attn_desc;
 
 /* Operation codes for ea_workspace_bytes. */
@@ -108,8 +111,10 @@ int32_t ea_mask_words(const ea_attn_desc* desc);
  *   w_J     = max(1, floor(P[I, J] * 2^24 + 1/2)),
  *   select  the shortest prefix of J sorted by (w desc, J asc) whose integer
  *           mass reaches tau * sum_J w_J, then add J = 0 and J = I.
- * Each q-head scores and selects its own mask; XA runs on sequences whose
- * length is a multiple of B.  On an XA head of a sequence with L % B != 0,
+ * Each q-head scores and selects its own mask (xa_group = 0), or every KV
+ * head scores once with s^ averaged over its q-heads and all of them get that
+ * mask (xa_group = 1: one reading of per-KV-head selection); XA runs on
+ * sequences whose length is a multiple of B.  On an XA head of a sequence with L % B != 0,
  * every causal block is selected (XA with tau = 1, which is FA).
  *
  * Inputs  q [T,Hq,d] bf16, k [T,Hkv,d] bf16, cu_seqlens_dev int32[num_seqs+1],

@@ -33,6 +33,8 @@ class Config:
     xa_stride: int = 8
     tau_num: int = 9
     tau_den: int = 10
+    # XA masks: 0 = one per q-head; 1 = one per KV head (group-mean scores).
+    xa_group: int = 0
     # Fixed sequence lengths, or None when they are drawn from the seed
     # (ragged batch: `ragged_count` lengths, each block * U{lo..hi}).
     seqlens: Optional[Tuple[int, ...]] = None
@@ -100,6 +102,13 @@ CONFIGS = {
         seqlens=(65536,), modes=_row(xa=(0, 4)), sparse_mode=MODE_SSA,
         needle_layout="clustered", needle_blocks_per_64k=16,
         description="batch 1, seq 65536, 32/8 heads, d 128, XA {0,4} (block 128, stride 8, tau 0.9) + 6 SSA (sink 128, window 4096)"),
+    # The same XA-SSA layer with one XA mask per KV head (group-mean scores).
+    "xassa-64k-group": Config(
+        name="xassa-64k-group", seed=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block=128, ssa_sink=128, ssa_window=4096, xa_stride=8, xa_group=1,
+        seqlens=(65536,), modes=_row(xa=(0, 4)), sparse_mode=MODE_SSA,
+        needle_layout="clustered", needle_blocks_per_64k=16,
+        description="batch 1, seq 65536, 32/8 heads, d 128, XA {0,4} (block 128, stride 8, tau 0.9, one mask per KV head) + 6 SSA (sink 128, window 4096)"),
     # The same XA-SSA layer with the XA parameters of the pages' Table 8:
     # block 64 and stride 16 (4 reduced rows per block); kernel tiles of 64.
     "xassa-64k-b64s16": Config(

@@ -76,7 +76,12 @@ def oracle_xa(inp, pairs=None, rows=None):
                 continue
             if pairs is not None and (b, h) not in pairs:
                 continue
-            qh = widen_head(inp, "q", b, h)
+            if getattr(cfg, "xa_group", 0):
+                # One mask per KV head: scored with the group-mean query.
+                qh = OX.group_query([widen_head(inp, "q", b, hg)
+                                     for hg in range((h // G) * G, (h // G + 1) * G)])
+            else:
+                qh = widen_head(inp, "q", b, h)
             kg = widen_head(inp, "k", b, h // G)
             r = None if rows is None else rows.get((b, h))
             res[(b, h)] = OX.head_mask(qh, kg, cfg.xa_stride, cfg.block, cfg.softmax_scale,

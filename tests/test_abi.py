@@ -70,6 +70,8 @@ BAD = [
     (dict(max_seqlen=5000), E.EA_ERR_INVALID_ARG),          # longer than the batch
     (dict(num_seqs=2, max_seqlen=1000), E.EA_ERR_INVALID_ARG),  # 2 * 1000 < 4096
     (dict(num_seqs=0), E.EA_ERR_INVALID_ARG),
+    (dict(xa_group=2), E.EA_ERR_INVALID_ARG),
+    (dict(xa_group=1, num_q_heads=64), E.EA_ERR_UNSUPPORTED),   # G = 8: one mask per KV head needs G <= 4
 ]
 
 

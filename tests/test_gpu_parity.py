@@ -315,3 +315,26 @@ def test_qwen8b_faxa_256k_sampled():
 
 def test_qwen8b_xassa_256k_sampled():
     _sampled_check("qwen8b-xassa-256k", 96, 4, xa_rows_per_head=3)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 4), (4, 4)])
+def test_xa_one_mask_per_kv_head(hq, hkv):
+    # xa_group = 1: every q-head of an XA KV head gets the mask selected from
+    # the group-mean antidiagonal scores; masks equal across the group, parity
+    # with the oracle's group reading, and the attention on those masks.
+    cfg = _small(name="xa-group", seqlens=(1024, 640, 384), num_q_heads=hq, num_kv_heads=hkv,
+                 modes=tuple(tuple(MODE_XA if (b + g) % 3 != 2 else MODE_SSA for g in range(hkv))
+                             for b in range(3)),
+                 xa_group=1, needle_layout="clustered", needle_blocks_per_64k=512)
+    inp = make_inputs(cfg)
+    gout, masks, stats = _full_check(inp, f"xa group Hq {hq} Hkv {hkv}")
+    G = cfg.gqa
+    m = gout["mask"].reshape(-1, hq, gout["mask"].shape[-1])
+    nrows = int(PU.qb_prefix(inp["seqlens"], cfg.block)[-1])
+    for g in range(hkv):
+        for u in range(1, G):
+            assert np.array_equal(m[:nrows, g * G], m[:nrows, g * G + u])
+
+
+def test_xassa_64k_group_sampled():
+    _sampled_check("xassa-64k-group", 192, 7)

@@ -23,6 +23,7 @@ static ea_status make_dims(const ea_attn_desc* desc, EaDims* d) {
       a.xa_tau_den > (1 << 20))
     return EA_ERR_INVALID_ARG;
   if (a.xa_group != 0 && a.xa_group != 1) return EA_ERR_INVALID_ARG;
+  if (a.xa_norm != 0 && a.xa_norm != 1) return EA_ERR_INVALID_ARG;
   if (a.head_dim != 64 && a.head_dim != 128) return EA_ERR_UNSUPPORTED;
   if (a.block != 64 && a.block != 128) return EA_ERR_UNSUPPORTED;
   if (a.block % a.xa_stride) return EA_ERR_INVALID_ARG;
@@ -38,6 +39,7 @@ static ea_status make_dims(const ea_attn_desc* desc, EaDims* d) {
   d->ngr = d->G / d->hpw;
   d->xa_hpi = (d->G % 4 == 0) ? 4 : (d->G % 2 == 0) ? 2 : 1;
   d->xa_group = a.xa_group;
+  d->xa_norm = a.xa_norm;
   if (a.xa_group && d->xa_hpi != d->G) return EA_ERR_UNSUPPORTED;
   d->D = a.head_dim;
   d->B = a.block;

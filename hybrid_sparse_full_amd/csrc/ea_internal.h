@@ -21,6 +21,7 @@ struct EaDims {
   int32_t ngr;      // head groups per KV head: G / hpw
   int32_t xa_hpi;   // q-heads per XA scoring item (4, 2 or 1; divides G)
   int32_t xa_group; // 1: one XA mask per KV head (xa_hpi == G)
+  int32_t xa_norm;  // 1: P from the raw block sums (softmax per block row)
   float scale;
   int32_t sink, window, tau_num, tau_den;
   int64_t nqb_max;  // bound on sum_b ceil(L_b / B):  T / B + nseq

@@ -69,6 +69,8 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
   const int64_t total = pair_items[npairs];
   unsigned long long* ctr = (unsigned long long*)(m.scal + SCAL_CTR64);
   const float C2 = d.scale * LOG2E * (GROUP ? 1.0f / HPI : 1.0f);
+  const float Cs = d.scale * (GROUP ? 1.0f / HPI : 1.0f);  // natural units (block sums)
+  const bool raw_sums = d.xa_norm != 0;
   const int S = d.S;
   const int nhg = d.Hq / HPI;
   const int nst = S * D / C::KC;
@@ -226,16 +228,27 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
               v[e] = ok ? acc[i][j][r] : -INFINITY;
               mloc = fmaxf(mloc, v[e]);
             }
-            const float mm = R >= 8 ? halves_max(mloc) : mloc;
-            float sum = 0.f;
-            if (FULL || mm != -INFINITY) {
+            float out;
+            if (__builtin_expect(raw_sums, 0)) {
+              // Block-sum masses: the plain sum of the allowed scores.
+              float sr = 0.f;
 #pragma unroll
-              for (int e = 0; e < RPG; ++e) sum += __builtin_amdgcn_exp2f((v[e] - mm) * C2);
+              for (int e = 0; e < RPG; ++e) sr += v[e] == -INFINITY ? 0.f : v[e];
+              if (R >= 8) sr = halves_sum(sr);
+              out = sr * Cs;
+            } else {
+              const float mm = R >= 8 ? halves_max(mloc) : mloc;
+              float sum = 0.f;
+              if (FULL || mm != -INFINITY) {
+#pragma unroll
+                for (int e = 0; e < RPG; ++e) sum += __builtin_amdgcn_exp2f((v[e] - mm) * C2);
+              }
+              if (R >= 8) sum = halves_sum(sum);
+              out = mm * C2 + __builtin_amdgcn_logf(sum);
             }
-            if (R >= 8) sum = halves_sum(sum);
             if ((R < 8 || half == 0) && (FULL || (a < nred && J <= Ia))) {
               const int64_t idx = base_bh + (int64_t)R * tri64(Ia) + (int64_t)(a - R * Ia) * (Ia + 1) + J;
-              lse_ws[idx] = mm * C2 + __builtin_amdgcn_logf(sum);
+              lse_ws[idx] = out;
             }
           }
         }
@@ -301,9 +314,29 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
   const float* base =
       lse_ws + (int64_t)R * (m.tri_prefix[b] * d.Hq + (int64_t)hs * tri64(nqb)) + (int64_t)R * tri64(I);
   // 1. Per reduced row a: La = log2 sum_J exp2(lse2[a, J]), one online pass
-  //    (lane-local running max and sum, then merged over the wave).
+  //    (lane-local running max and sum, then merged over the wave).  With
+  //    block-sum masses the workspace holds per-row partial sums of s^
+  //    instead, and one log-sum-exp over J of their column sums serves the row.
   float La[R];
-  {
+  float Lraw = 0.f;
+  const bool raw_sums = d.xa_norm != 0;
+  if (__builtin_expect(raw_sums, 0)) {
+    float mr = -INFINITY, zr = 0.f;
+    for (int J = lane; J < nI; J += 64) {
+      float raw = 0.f;
+#pragma unroll
+      for (int a = 0; a < R; ++a) raw += base[(int64_t)a * nI + J];
+      const float x = raw * LOG2E;
+      const float mn = fmaxf(mr, x);
+      zr = zr * __builtin_amdgcn_exp2f(mr - mn) + __builtin_amdgcn_exp2f(x - mn);
+      mr = mn;
+    }
+    const float mx = wave_max(mr);
+    const float z = wave_sum(mr == -INFINITY ? 0.f : zr * __builtin_amdgcn_exp2f(mr - mx));
+    Lraw = mx + __builtin_amdgcn_logf(z);
+#pragma unroll
+    for (int a = 0; a < R; ++a) La[a] = 0.f;
+  } else {
     float mr[R], zr[R];
 #pragma unroll
     for (int a = 0; a < R; ++a) {
@@ -339,10 +372,18 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
   float* bm = block_mass ? block_mass + row * d.maxqb : nullptr;
 #pragma unroll 2
   for (int J = lane; J < nI; J += 64) {
-    float acc = 0.f;
+    float P;
+    if (__builtin_expect(raw_sums, 0)) {
+      float raw = 0.f;
 #pragma unroll
-    for (int a = 0; a < R; ++a) acc += __builtin_amdgcn_exp2f(base[(int64_t)a * nI + J] - La[a]);
-    const float P = acc * (1.0f / R);
+      for (int a = 0; a < R; ++a) raw += base[(int64_t)a * nI + J];
+      P = __builtin_amdgcn_exp2f(raw * LOG2E - Lraw);
+    } else {
+      float acc = 0.f;
+#pragma unroll
+      for (int a = 0; a < R; ++a) acc += __builtin_amdgcn_exp2f(base[(int64_t)a * nI + J] - La[a]);
+      P = acc * (1.0f / R);
+    }
     if (bm) bm[J] = P;
     const float x = P * 16777216.0f;
     const float fl = floorf(x);

@@ -52,7 +52,7 @@ class AttnDesc(ctypes.Structure):
         ("block", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("ssa_sink", ctypes.c_int32), ("ssa_window", ctypes.c_int32),
         ("xa_stride", ctypes.c_int32), ("xa_tau_num", ctypes.c_int32),
-        ("xa_tau_den", ctypes.c_int32), ("xa_group", ctypes.c_int32),
+        ("xa_tau_den", ctypes.c_int32), ("xa_group", ctypes.c_int32), ("xa_norm", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -18,13 +18,13 @@ from . import ea as E
 
 def make_desc(*, num_seqs, total_tokens, max_seqlen, num_q_heads, num_kv_heads, head_dim,
               block, softmax_scale=None, ssa_sink=128, ssa_window=2048, xa_stride=8,
-              xa_tau=(9, 10), xa_group=0):
+              xa_tau=(9, 10), xa_group=0, xa_norm=0):
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
     return E.AttnDesc(int(num_seqs), int(total_tokens), int(max_seqlen), int(num_q_heads),
                       int(num_kv_heads), int(head_dim), int(block), float(softmax_scale),
                       int(ssa_sink), int(ssa_window), int(xa_stride), int(xa_tau[0]),
-                      int(xa_tau[1]), int(xa_group))
+                      int(xa_tau[1]), int(xa_group), int(xa_norm))
 
 
 class Router:
@@ -175,4 +175,5 @@ def desc_for(cfg, seqlens):
                      num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
                      head_dim=cfg.head_dim, block=cfg.block, softmax_scale=cfg.softmax_scale,
                      ssa_sink=cfg.ssa_sink, ssa_window=cfg.ssa_window, xa_stride=cfg.xa_stride,
-                     xa_tau=(cfg.tau_num, cfg.tau_den), xa_group=cfg.xa_group)
+                     xa_tau=(cfg.tau_num, cfg.tau_den), xa_group=cfg.xa_group,
+                     xa_norm=cfg.xa_norm)

@@ -72,6 +72,9 @@ typedef struct {
   int32_t xa_group;      /* 0: one XA mask per q-head; 1: one per KV head, scored
                             with the mean of its q-heads' antidiagonal scores
                             (needs Hq / Hkv in {1, 2, 4}) */
+  int32_t xa_norm;       /* 0: softmax per reduced query row, pooled into
+                            blocks (default); 1: softmax over each block row of
+                            the raw block sums of s^ (for comparison) */
 } ea_attn_desc;
 
 /* Operation codes for ea_workspace_bytes. */
@@ -107,7 +110,9 @@ int32_t ea_mask_words(const ea_attn_desc* desc);
  *   score   s^[a, b'] = c * sum_{t<S} <q_{aS+t}, k_{b'S+S-1-t}>  for b' <= a
  *           (a, b' index groups of S tokens inside the sequence),
  *   p[a, .] = softmax over b' <= a of s^[a, .],
- *   P[I, J] = (1 / (B/S)) * sum of p over the (a, b') pairs of block (I, J),
+ *   P[I, J] = (1 / (B/S)) * sum of p over the (a, b') pairs of block (I, J)
+ *             (xa_norm = 1 instead: P[I, .] = softmax over J <= I of the sums
+ *             of s^ over the causal (a, b') pairs of block (I, J)),
  *   w_J     = max(1, floor(P[I, J] * 2^24 + 1/2)),
  *   select  the shortest prefix of J sorted by (w desc, J asc) whose integer
  *           mass reaches tau * sum_J w_J, then add J = 0 and J = I.

@@ -171,7 +171,7 @@ def group_query(q_group):
     return np.asarray(q_group, dtype=np.float64).mean(axis=0)
 
 
-def head_mask(qh, kg, S, B, scale, tau_num, tau_den, rows=None):
+def head_mask(qh, kg, S, B, scale, tau_num, tau_den, rows=None, normalization="R2"):
     """XA block mask of one (sequence, q-head) and its block masses.
 
     A sequence whose length is not a whole number of blocks gets every causal
@@ -182,5 +182,5 @@ def head_mask(qh, kg, S, B, scale, tau_num, tau_den, rows=None):
     nb = -(-L // B)
     if L % B:
         return np.tril(np.ones((nb, nb), dtype=bool)), None
-    P = block_mass(qh, kg, S, B, scale, rows=rows)
+    P = block_mass(qh, kg, S, B, scale, normalization=normalization, rows=rows)
     return select(P, tau_num, tau_den, rows=rows), P

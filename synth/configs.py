@@ -35,6 +35,9 @@ class Config:
     tau_den: int = 10
     # XA masks: 0 = one per q-head; 1 = one per KV head (group-mean scores).
     xa_group: int = 0
+    # XA block masses: 0 = softmax per reduced row then pooled (R2);
+    # 1 = softmax over each block row of the raw block sums (R1).
+    xa_norm: int = 0
     # Fixed sequence lengths, or None when they are drawn from the seed
     # (ragged batch: `ragged_count` lengths, each block * U{lo..hi}).
     seqlens: Optional[Tuple[int, ...]] = None
@@ -109,6 +112,14 @@ CONFIGS = {
         seqlens=(65536,), modes=_row(xa=(0, 4)), sparse_mode=MODE_SSA,
         needle_layout="clustered", needle_blocks_per_64k=16,
         description="batch 1, seq 65536, 32/8 heads, d 128, XA {0,4} (block 128, stride 8, tau 0.9, one mask per KV head) + 6 SSA (sink 128, window 4096)"),
+    # The same XA-SSA layer with the block masses taken from the raw block
+    # sums (reading R1, for comparison).
+    "xassa-64k-r1": Config(
+        name="xassa-64k-r1", seed=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block=128, ssa_sink=128, ssa_window=4096, xa_stride=8, xa_norm=1,
+        seqlens=(65536,), modes=_row(xa=(0, 4)), sparse_mode=MODE_SSA,
+        needle_layout="clustered", needle_blocks_per_64k=16,
+        description="batch 1, seq 65536, 32/8 heads, d 128, XA {0,4} (block 128, stride 8, tau 0.9, R1 block sums) + 6 SSA (sink 128, window 4096)"),
     # The same XA-SSA layer with the XA parameters of the pages' Table 8:
     # block 64 and stride 16 (4 reduced rows per block); kernel tiles of 64.
     "xassa-64k-b64s16": Config(

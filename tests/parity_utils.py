@@ -85,7 +85,8 @@ def oracle_xa(inp, pairs=None, rows=None):
             kg = widen_head(inp, "k", b, h // G)
             r = None if rows is None else rows.get((b, h))
             res[(b, h)] = OX.head_mask(qh, kg, cfg.xa_stride, cfg.block, cfg.softmax_scale,
-                                       cfg.tau_num, cfg.tau_den, rows=r)
+                                       cfg.tau_num, cfg.tau_den, rows=r,
+                                       normalization="R1" if getattr(cfg, "xa_norm", 0) else "R2")
     return res
 
 

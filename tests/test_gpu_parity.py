@@ -338,3 +338,19 @@ def test_xa_one_mask_per_kv_head(hq, hkv):
 
 def test_xassa_64k_group_sampled():
     _sampled_check("xassa-64k-group", 192, 7)
+
+
+@pytest.mark.parametrize("group", [0, 1])
+def test_xa_block_sum_masses(group):
+    # xa_norm = 1 (reading R1): P is the softmax over each block row of the
+    # raw block sums of s^; per q-head and per KV head.
+    cfg = _small(name="xa-r1", seqlens=(1024, 640), num_q_heads=8, num_kv_heads=2,
+                 modes=((MODE_XA, MODE_SSA), (MODE_XA, MODE_XA)), xa_norm=1, xa_group=group,
+                 needle_layout="clustered", needle_blocks_per_64k=512)
+    inp = make_inputs(cfg)
+    gout, masks, stats = _full_check(inp, f"xa R1 group {group}")
+    assert stats["rows"] > 0
+
+
+def test_xassa_64k_r1_sampled():
+    _sampled_check("xassa-64k-r1", 192, 5)

@@ -77,6 +77,9 @@ size_t ws_layout(const EaDims& d, int op, WsLayout* L) {
   L->qb2seq = take(4 * (size_t)d.nqb_max);
   L->scal = take(4 * (size_t)SCAL_COUNT);
   if (op == EA_OP_DECODE) {
+    if (decode_waves(d) > 0x7fffffff) return 0;  // rejected by the decode call
+    L->dec_plan = take(8);
+    L->dec_waves = take(8 * (size_t)decode_waves(d));
     L->dec_part = take(4 * (size_t)d.nseq * d.Hq * (size_t)decode_splits(d) * (d.D + 2));
     L->total = off;
     return off;
@@ -286,12 +289,13 @@ ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, con
       ((uintptr_t)lse_out_dev & 3u))
     return EA_ERR_INVALID_ARG;
   if (d.nseq > 65535 || d.Hkv > 65535) return EA_ERR_UNSUPPORTED;
+  if (decode_waves(d) > 0x7fffffff) return EA_ERR_UNSUPPORTED;
   WsLayout L;
   const size_t need = ws_layout(d, EA_OP_DECODE, &L);
   if (!workspace_dev || workspace_bytes < need) return EA_ERR_WORKSPACE;
   if (d.nseq == 0) return EA_OK;
   if (launch_decode(d, (const uint16_t*)q_dev, (const uint16_t*)k_dev, (const uint16_t*)v_dev,
-                    cu_seqlens_dev, modes_dev, (char*)workspace_dev + L.dec_part,
+                    cu_seqlens_dev, modes_dev, workspace_dev, L,
                     (uint16_t*)o_out_dev, lse_out_dev, (hipStream_t)stream) != hipSuccess)
     return EA_ERR_HIP;
   return EA_OK;

@@ -9,11 +9,17 @@
 // q-head, ~4 flop per byte: it is bound by HBM bandwidth, so it runs on the
 // vector ALU with bf16 dot products, not on the matrix core.  Design:
 //   * split-K over waves: one wave takes a split of 256 to 4096 kept-key
-//     positions (sized from the descriptor) of one (sequence, KV head) for
+//     positions of one (sequence, KV head) for
 //     GW of its q-heads (all G when G <= 8), so each
 //     K/V row is read once per GW heads.  The key set is compressed: an SSA
 //     head's first split covers the sink and the start of the window.
-//     Waves are independent: no LDS staging and no workgroup barrier;
+//     The split length comes from the kept keys of the whole step: when the
+//     modes could change it, a one-workgroup plan kernel sums them, picks
+//     the split and lists the waves that have work, so a step whose heads
+//     are mostly SSA still spreads over as many waves as an all-FA one, and
+//     no idle wave sits between busy ones in the grid (the rest of the grid,
+//     sized for the shortest split, ends at once).  Waves are independent:
+//     no LDS staging and no workgroup barrier;
 //   * lane layout: a key row of d bf16 is spread over d / 8 lanes, 16 bytes
 //     each, so one wave load moves 64 / (d / 8) whole rows (contiguous 2 d
 //     bytes per row) of K and of V;
@@ -41,6 +47,8 @@ struct DecArgs {
   const int32_t* cu;
   const uint8_t* modes;
   float* part;         // [nseq, Hq, nsplit_max, D + 2]
+  const int32_t* plan;  // null: split is fixed; else [0] split, [1] listed waves
+  const int2* wlist;    // (unit, split) per listed wave, unit = (b Hkv + g) (G / GW) + wg
   int32_t nseq, Hq, Hkv, G, T, maxL, sink, window, split, nsplit_max;
   float c2;            // softmax scale * log2(e)
 };
@@ -96,30 +104,108 @@ __device__ inline float groups_sum(float x) {
   return halves_sum(x);
 }
 
+__device__ inline int32_t dec_split(const DecArgs& a) { return a.plan ? a.plan[0] : a.split; }
+
+// Kept keys of (sequence, KV head) i = b * Hkv + g.
+__device__ inline int32_t dec_kept_at(const DecArgs& a, int64_t i) {
+  int32_t s0, L;
+  seq_bounds(a, (int)(i / a.Hkv), &s0, &L);
+  int mode = sane_mode(a.modes[i]);
+  if (mode == EA_MODE_XA) mode = EA_MODE_FA;
+  return dec_kept(mode, L, a.sink, a.window);
+}
+
+// Plan of one decode step, one workgroup: the split (decode_split_rule over
+// the kept keys of every (sequence, KV head) times the nwg head groups, no
+// lower than s_min), then one wlist entry per wave that has work, units in
+// order, so those waves are a prefix of the grid.  plan[0] = split,
+// plan[1] = listed waves.  The list holds at most (units) * ceil(maxL /
+// s_min) entries, the grid's size.
+__global__ __launch_bounds__(1024) void k_decode_plan(DecArgs a, int32_t s_min, int32_t nwg,
+                                                      int32_t* plan, int2* wlist) {
+  __shared__ long long red[16];
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t s_split;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t nbg = (int64_t)a.nseq * a.Hkv;
+  long long w = 0;
+  for (int64_t i = tid; i < nbg; i += 1024) w += dec_kept_at(a, i);
+  for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off);
+  if (lane == 0) red[wv] = w;
+  __syncthreads();
+  if (tid == 0) {
+    long long t = 0;
+    for (int i = 0; i < 16; ++i) t += red[i];
+    s_split = decode_split_rule((int64_t)t * nwg, s_min);
+  }
+  __syncthreads();
+  const int32_t S = s_split;
+  // Exclusive scan of the per-unit split counts, 1024 units at a time.
+  const int64_t nu = nbg * nwg;
+  int32_t base = 0;
+  for (int64_t c0 = 0; c0 < nu; c0 += 1024) {
+    const int64_t u = c0 + tid;
+    const int32_t cnt = u < nu ? cdiv(dec_kept_at(a, u / nwg), S) : 0;
+    int32_t x = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int32_t before = 0, total = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int32_t v = wsum[i];
+      before += i < wv ? v : 0;
+      total += v;
+    }
+    const int32_t first = base + before + x - cnt;
+    for (int32_t j = 0; j < cnt; ++j) wlist[first + j] = make_int2((int)u, j);
+    base += total;
+    __syncthreads();  // wsum is rewritten by the next chunk
+  }
+  if (tid == 0) {
+    plan[0] = S;
+    plan[1] = base;
+  }
+}
+
 template <int D, int GW>
 __global__ __launch_bounds__(256) void k_decode(DecArgs a) {
   constexpr int LPK = D / 8;          // lanes per key row
   constexpr int KPI = 64 / LPK;       // keys per wave iteration
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPK, pc = lane % LPK;
-  // Wave -> (split, head group, KV head, sequence); split fastest.
+  // Wave -> (split, head group, KV head, sequence): from the plan's list,
+  // else split fastest.
   const int nwg = a.G / GW;
-  int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int split = (int)(w % a.nsplit_max);
-  w /= a.nsplit_max;
-  const int wg = (int)(w % nwg);
-  w /= nwg;
-  const int g = (int)(w % a.Hkv);
-  const int b = (int)(w / a.Hkv);
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int32_t S, split;
+  int64_t u;
+  if (a.plan) {
+    S = a.plan[0];
+    if (w >= a.plan[1]) return;  // wave-uniform
+    const int2 e = a.wlist[w];
+    u = e.x;
+    split = e.y;
+  } else {
+    S = a.split;
+    split = (int)(w % a.nsplit_max);
+    u = w / a.nsplit_max;
+  }
+  const int wg = (int)(u % nwg);
+  u /= nwg;
+  const int g = (int)(u % a.Hkv);
+  const int b = (int)(u / a.Hkv);
   if (b >= a.nseq) return;
   int32_t s0, L;
   seq_bounds(a, b, &s0, &L);
   int mode = sane_mode(a.modes[(size_t)b * a.Hkv + g]);
   if (mode == EA_MODE_XA) mode = EA_MODE_FA;
   const int32_t n = dec_kept(mode, L, a.sink, a.window);
-  const int32_t p0 = split * a.split;
+  const int32_t p0 = split * S;
   if (p0 >= n) return;  // wave-uniform
-  const int32_t p1 = min(n, p0 + a.split);
+  const int32_t p1 = p0 + min(S, n - p0);
   const int nit = (p1 - p0 + KPI - 1) / KPI;
   const int nblk = (nit + DEC_BI - 1) / DEC_BI;
   const int h0 = g * a.G + wg * GW;
@@ -257,7 +343,8 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecArgs a, uint16_t* out
   int mode = sane_mode(a.modes[(size_t)b * a.Hkv + h / a.G]);
   if (mode == EA_MODE_XA) mode = EA_MODE_FA;
   const int32_t n = dec_kept(mode, L, a.sink, a.window);
-  const int ns = (n + a.split - 1) / a.split;
+  const int32_t S = dec_split(a);
+  const int ns = cdiv(n, S);
   const float* src = a.part + ((size_t)b * a.Hq + h) * a.nsplit_max * (D + 2);
   float M = -INFINITY;
   for (int s = tid; s < ns; s += 256) M = fmaxf(M, src[(size_t)s * (D + 2) + D]);
@@ -294,15 +381,15 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecArgs a, uint16_t* out
 }
 
 hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* cu, const uint8_t* modes, void* ws, uint16_t* o, float* lse,
-                         hipStream_t st) {
+                         const int32_t* cu, const uint8_t* modes, void* ws, const WsLayout& L,
+                         uint16_t* o, float* lse, hipStream_t st) {
   DecArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.cu = cu;
   a.modes = modes;
-  a.part = (float*)ws;
+  a.part = (float*)((char*)ws + L.dec_part);
   a.nseq = d.nseq;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
@@ -311,12 +398,23 @@ hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, 
   a.maxL = d.maxL;
   a.sink = d.sink;
   a.window = d.window;
-  a.split = decode_split(d);
+  // Splits of at least decode_split_min: the partials hold nsplit_max of them
+  // per (sequence, q-head) and the grid one wave each.
+  const int gw = decode_gw(d);
+  a.split = decode_split_min(d);
   a.nsplit_max = decode_splits(d);
+  a.plan = nullptr;
+  a.wlist = nullptr;
   a.c2 = d.scale * LOG2E;
+  if (a.nsplit_max > 0 && decode_split_max(d) > a.split) {
+    int32_t* plan = (int32_t*)((char*)ws + L.dec_plan);
+    int2* wlist = (int2*)((char*)ws + L.dec_waves);
+    hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, st, a, a.split, d.G / gw, plan, wlist);
+    a.plan = plan;
+    a.wlist = wlist;
+  }
   if (a.nsplit_max > 0) {
-    const int gw = decode_gw(d);
-    const int64_t waves = (int64_t)d.nseq * d.Hkv * (d.G / gw) * a.nsplit_max;
+    const int64_t waves = decode_waves(d);
     const dim3 grid((unsigned)((waves + 3) / 4));
     void (*kern)(DecArgs) = nullptr;
     if (d.D == 128)

@@ -51,6 +51,11 @@ enum {
   SCAL_COUNT = 16
 };
 
+// ---- helpers usable on host and device ----
+__host__ __device__ inline int64_t tri64(int64_t n) { return n * (n + 1) / 2; }
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (no overflow near 2^31).
+__host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return a / b + (a % b != 0 ? 1 : 0); }
+
 // Byte offsets of every workspace buffer (256-byte aligned).
 struct WsLayout {
   size_t seq_start, seq_len, qb_prefix, tri_prefix, qb2seq, scal;
@@ -59,7 +64,7 @@ struct WsLayout {
   // prefill
   size_t kvp, unit_cost, row_cost, row_off, hist, cursor, sorted_units, tiles;
   // decode
-  size_t dec_part;
+  size_t dec_plan, dec_waves, dec_part;
   size_t total;
 };
 
@@ -80,30 +85,47 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v
                            const WsLayout& L, hipStream_t st);
 hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint8_t* modes, const SeqMeta& m, void* ws,
                             const WsLayout& L, uint16_t* o, float* lse, hipStream_t st);
-// Decode: kept-key positions per split (one wave each), chosen from the
-// descriptor alone so that an all-FA step would spread over about 2048
-// waves (8 per CU): a power of two in [256, 4096].  Longer splits amortise a
-// wave's pipeline start; more splits fill the chip when the batch is small.
+// Decode: kept-key positions per split (one wave each), a power of two in
+// [256, 4096].  The rule: the smallest split s with s * DEC_WAVES >= the
+// step's work, where work = sum over (sequence, KV head) of its kept keys
+// times the q-head groups per KV head (G / gw), so the step spreads over
+// about DEC_WAVES waves (8 per CU).  Longer splits amortise a wave's
+// pipeline start; more splits fill the chip when the batch is small.
+// The kept keys depend on the modes, which live in device memory: the host
+// bounds the work by the all-FA case (T keys per KV head), which gives the
+// largest split.  When that bound leaves a choice, k_decode_plan applies the
+// rule to the true work on the device (no lower than an eighth of the bound)
+// and lists the waves that have work, so no idle wave sits between them.
+// The grid, the wave list and the partials are sized for the smallest split.
+constexpr int32_t DEC_WAVES = 2048;
 inline int32_t decode_gw(const EaDims& d) {
   return d.G % 8 == 0 ? 8 : d.G % 4 == 0 ? 4 : d.G % 2 == 0 ? 2 : 1;
 }
-inline int32_t decode_split(const EaDims& d) {
-  const int64_t work = (int64_t)d.T * d.Hkv * (d.G / decode_gw(d));
-  int32_t s = 256;
-  while (s < 4096 && (int64_t)s * 2048 < work) s *= 2;
+__host__ __device__ inline int32_t decode_split_rule(int64_t work, int32_t s) {
+  while (s < 4096 && (int64_t)s * DEC_WAVES < work) s *= 2;
   return s;
 }
-inline int32_t decode_splits(const EaDims& d) { return (d.maxL + decode_split(d) - 1) / decode_split(d); }
+inline int32_t decode_split_max(const EaDims& d) {
+  return decode_split_rule((int64_t)d.T * d.Hkv * (d.G / decode_gw(d)), 256);
+}
+inline int32_t decode_split_min(const EaDims& d) {
+  const int32_t s = decode_split_max(d) / 8;
+  return s < 256 ? 256 : s;
+}
+inline int32_t decode_splits(const EaDims& d) { return cdiv(d.maxL, decode_split_min(d)); }
+// Waves of the decode grid: one per (split, head group, KV head, sequence),
+// saturated at 2^62 (the decode call rejects more than 2^31 - 1).
+inline int64_t decode_waves(const EaDims& d) {
+  const double w = (double)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_splits(d);
+  return w >= 4.6e18 ? ((int64_t)1 << 62) : (int64_t)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_splits(d);
+}
 hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* cu, const uint8_t* modes, void* ws, uint16_t* o, float* lse,
-                         hipStream_t st);
+                         const int32_t* cu, const uint8_t* modes, void* ws, const WsLayout& L,
+                         uint16_t* o, float* lse, hipStream_t st);
 hipError_t launch_route(const EaDims& d, const ea_router_desc& w, const uint16_t* k,
                         const int32_t* cu, uint8_t retrieval_mode, uint8_t sparse_mode,
                         uint8_t* modes, float* logits, hipStream_t st);
 
-// ---- helpers usable on host and device ----
-__host__ __device__ inline int64_t tri64(int64_t n) { return n * (n + 1) / 2; }
-__host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 // Tile-list entry: kv-block index in bits 0..28, bit 31 = needs a token mask,
 // bits 29 and 30 = the first / second q-head of the row's head group attends

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(META_NT) void k_seq_meta(EaDims d, const int32_t* _
   //    start_b = max(clamp(cu[b]), max_{b' < b} end_b'), end_b = clamp(cu[b+1])
   //    with len_b <= max_seqlen: the sequences are disjoint and inside [0, T),
   //    whatever cu_seqlens holds, and equal to cu_seqlens when it is valid.
-  const int chunk = (nseq + META_NT - 1) / META_NT;
+  const int chunk = cdiv(nseq, META_NT);
   const int b0 = min(nseq, tid * chunk), b1 = min(nseq, b0 + chunk);
   int64_t emax = 0;
   for (int b = b0; b < b1; ++b) {

@@ -234,9 +234,13 @@ ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu_seqlens
  *         (sanitised on the device as for the prefill).
  * Outputs o_out_dev [num_seqs, Hq, d] bf16, lse_out_dev [num_seqs, Hq] fp32.
  * The descriptor's block / xa fields must be valid but are unused; Hq / Hkv
- * <= 16 (EA_ERR_UNSUPPORTED otherwise).
+ * <= 16, num_seqs and Hkv <= 65535, and at most 2^31 - 1 key-split waves
+ * (num_seqs * Hkv * ceil(max_seqlen / split) for the shortest split the
+ * descriptor allows) (EA_ERR_UNSUPPORTED otherwise).
  * Workspace: ea_workspace_bytes(desc, EA_OP_DECODE) bytes of device memory
- * (fp32 partial results of the key splits).
+ * (the step's split plan and wave list, fp32 partial results of the key
+ * splits).  The step runs in stream order; concurrent calls need separate
+ * workspaces.
  */
 ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
                                 const void* v_dev, const int32_t* cu_seqlens_dev,

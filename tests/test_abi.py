@@ -286,7 +286,8 @@ def test_decode_rejects_bad_arguments_and_sizes_workspace():
     d = desc()
     need = E.ea_workspace_bytes(d, E.EA_OP_DECODE)
     # fp32 partials: num_seqs * Hq * ceil(max_seqlen / split) * (d + 2) floats, plus
-    # metadata; 4096 tokens x 8 KV heads / 2048 waves -> split 256, 16 splits
+    # metadata and the wave list; 4096 tokens x 8 KV heads / 2048 waves -> split
+    # 256, 16 splits
     assert need >= 4 * 1 * 32 * 16 * 130
 
     def call(dd=None, **kw):
@@ -308,3 +309,24 @@ def test_decode_rejects_bad_arguments_and_sizes_workspace():
     empty = desc(num_seqs=0, total_tokens=0, max_seqlen=0)
     assert call(empty, q=None, k=None, v=None, o=None, lse=None,
                 n=E.ea_workspace_bytes(empty, E.EA_OP_DECODE)) == E.EA_OK
+    # More than 2^31 - 1 key-split waves: no workspace size, and the call says so.
+    huge = desc(num_seqs=65535, total_tokens=2 ** 31 - 1, max_seqlen=2 ** 31 - 1,
+                num_q_heads=16, num_kv_heads=16)
+    assert E.ea_workspace_bytes(huge, E.EA_OP_DECODE) == 0
+    assert call(huge) == E.EA_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_do_not_wrap_near_int32_max():
+    # 2^31 - 1 tokens in one or two sequences, a sink as long as the cache:
+    # every size is an honest upper bound (no int32 wrap in ceil-divisions).
+    T = 2 ** 31 - 1
+    for kw in (dict(num_seqs=2, num_q_heads=8, num_kv_heads=8),
+               dict(num_seqs=1, num_q_heads=32, num_kv_heads=8, ssa_sink=T)):
+        d = desc(total_tokens=T, max_seqlen=T, **kw)
+        hkv, hq = kw["num_kv_heads"], kw["num_q_heads"]
+        pre = E.ea_workspace_bytes(d, E.EA_OP_PREFILL)
+        assert 2 * 2 * hkv * 128 * T <= pre < 2 ** 60          # packed K and V^T
+        dec = E.ea_workspace_bytes(d, E.EA_OP_DECODE)
+        # fp32 partials of splits of at least 512 keys, per (sequence, q-head)
+        assert 4 * hq * (T // 4096) * 130 <= dec < 2 ** 40
+        assert 0 < E.ea_workspace_bytes(d, E.EA_OP_XA_SELECT) < 2 ** 60

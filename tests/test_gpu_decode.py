@@ -101,3 +101,18 @@ def test_decode_64k_batch():
                                 modes=((0, 1, 1, 0, 1, 1, 0, 1), (1, 1, 1, 1, 1, 1, 1, 1),
                                        (0, 0, 0, 0, 0, 0, 0, 0), (2, 1, 1, 2, 1, 1, 2, 1))))
     _check(inp, "decode 64K batch 4")
+
+
+@pytest.mark.parametrize("modes", ["random", "all-ssa", "all-fa"])
+def test_decode_split_from_kept_keys(modes):
+    # 64 KV heads over ~17K tokens: the descriptor allows splits of 256 to
+    # 1,024 keys, and the device picks one from the kept keys of the step
+    # (random modes land in between, all-SSA at the floor, all-FA at the top).
+    seqlens = (9000, 5000, 0, 20, 3000, 1)
+    kw = dict(num_q_heads=64, num_kv_heads=64, head_dim=128, seqlens=seqlens, seed=77)
+    if modes == "all-ssa":
+        kw["modes"] = tuple((MODE_SSA,) * 64 for _ in seqlens)
+    elif modes == "all-fa":
+        kw["modes"] = tuple((MODE_FA,) * 64 for _ in seqlens)
+    inp = make_inputs(_small(**kw))
+    _check(inp, f"decode split from kept keys, {modes}")

@@ -451,7 +451,12 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
       nv = t & 1;
       const bool mine = t < cnt && (ecur & mybit) != 0;
       bool kd = false, vd = false;  // this period's K / V^T DMA issued
+      // A wave issues its MFMA phase at raised priority, so the other wave's
+      // exponentials on the same SIMD fill the gaps between MFMA issues
+      // instead of delaying them (measured: 2 % shorter launches; raising the
+      // softmax instead made them 1.5 % longer).
       if (!LAG) {
+        __builtin_amdgcn_s_setprio(1);
         if (__builtin_expect(pend, 1)) {
           compute_pv((t - 1) & 1, true);
           kd = true;
@@ -459,15 +464,22 @@ void k_attn(EaDims d, const uint16_t* __restrict__ q, const uint16_t* __restrict
         if (__builtin_expect(mine, 1)) {
           compute_s(t & 1, true);
           vd = true;
+          __builtin_amdgcn_s_setprio(0);
           softmax(ecur, false);
         }
+        __builtin_amdgcn_s_setprio(0);
       } else {
         if (__builtin_expect(pend, 1)) {
           softmax(epend, true);
           kd = vd = true;
+          __builtin_amdgcn_s_setprio(1);
           compute_pv((t - 1) & 1, false);
         }
-        if (__builtin_expect(mine, 1)) compute_s(t & 1, false);
+        if (__builtin_expect(mine, 1)) {
+          __builtin_amdgcn_s_setprio(1);
+          compute_s(t & 1, false);
+        }
+        __builtin_amdgcn_s_setprio(0);
       }
       if (__builtin_expect(!kd, 0)) {
 #pragma unroll

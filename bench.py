@@ -45,6 +45,9 @@ def parse():
                     help="sequences of the decode measurement (0 skips it)")
     ap.add_argument("--decode-only", action="store_true",
                     help="measure only the decode step (for profiling)")
+    ap.add_argument("--decode-modes", metavar="DIGITS",
+                    help="with --decode-only: one mode digit per KV head (0 FA, 1 SSA, 2 XA) "
+                         "in place of the workload's, e.g. 11111111")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -307,8 +310,13 @@ def main():
     cfg = get_config(a.config)
     if a.decode_only:
         meta = make_inputs(cfg, with_values=False)
+        row = meta["modes"][0]
+        if a.decode_modes:
+            row = [int(c) for c in a.decode_modes if c.isdigit()]
+            if len(row) != len(a.decode_modes) or len(row) != cfg.num_kv_heads or max(row) > 2:
+                raise SystemExit(f"--decode-modes needs {cfg.num_kv_heads} digits in 0..2")
         torch.cuda.set_device(0)
-        r = decode_bench(cfg, meta["modes"][0], int(np.max(meta["seqlens"])), max(a.decode_batch, 1),
+        r = decode_bench(cfg, row, int(np.max(meta["seqlens"])), max(a.decode_batch, 1),
                          max(a.steps, 20), a.warmup)
         print(json.dumps({"metric": "decode step HBM GB/s (kept K/V, q, o)", "value": r["roofline"]["achieved"],
                           "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "decode": r}), flush=True)

@@ -116,3 +116,16 @@ def test_decode_split_from_kept_keys(modes):
         kw["modes"] = tuple((MODE_FA,) * 64 for _ in seqlens)
     inp = make_inputs(_small(**kw))
     _check(inp, f"decode split from kept keys, {modes}")
+
+
+def test_decode_plan_scans_several_chunks():
+    # 200 ragged sequences x 8 KV heads = 1,600 (sequence, KV head) units, so
+    # the plan's scan of per-unit split counts crosses a 1,024-unit chunk; the
+    # ~100K cached tokens make the device choose the split.
+    rng = np.random.default_rng(5)
+    seqlens = tuple(int(x) for x in rng.integers(0, 1000, size=200))
+    modes = tuple(tuple(int(m) for m in r) for r in rng.integers(0, 3, size=(200, 8)))
+    cfg = _small(name="decode-many", num_q_heads=32, num_kv_heads=8, head_dim=128, seqlens=seqlens,
+                 modes=modes, ssa_sink=16, ssa_window=200, seed=9)
+    assert sum(seqlens) * 8 > 256 * 2048
+    _check(make_inputs(cfg), "decode 200 sequences")

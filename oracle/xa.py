@@ -35,7 +35,10 @@ tie-break are readings, not fixed by the pages (as is the optional
 one-mask-per-KV-head variant, group_query); they are pinned only by
 self-consistency (q = 0 closed form, brute-force antidiagonal enumeration,
 row normalization, subset brute force of the selector) -- parity unpinned by
-the pages themselves.
+the pages themselves.  The R1 masses are pinned by explicit enumeration of the
+block sums; kept_pairs by a token-by-token count; tie_info by hand-built rows
+on both sides of its thresholds; the partial-block rule of head_mask by its
+identity with FA.
 """
 
 import numpy as np
@@ -151,15 +154,21 @@ def tie_info(P_row, I, tau_num, tau_den, cum_eps=1e-4, gap_rel=1e-5):
 
 
 def kept_pairs(mask, L, B):
-    """Attended (i, j) pairs of one XA head: selected blocks, causal inside."""
+    """Attended (i, j) pairs of one XA (sequence, q-head) of length L.
+
+    For every selected block pair (I, J) with J <= I: the pairs with query i in
+    block I and key j in block J, both inside the sequence, and j <= i (the
+    causal rule inside the diagonal block).  A full block below the diagonal
+    gives B * B pairs, a full diagonal block B (B + 1) / 2, and a block cut by
+    the sequence end fewer.
+    """
     nb = mask.shape[0]
     total = 0
     for I in range(nb):
+        i = np.arange(I * B, min((I + 1) * B, L), dtype=np.int64)
         for J in np.nonzero(mask[I, : I + 1])[0]:
-            if J < I:
-                total += B * B
-            else:
-                total += B * (B + 1) // 2
+            j0, j1 = int(J) * B, min((int(J) + 1) * B, L)
+            total += int(np.clip(np.minimum(i, j1 - 1) - j0 + 1, 0, None).sum())
     return total
 
 
@@ -174,9 +183,10 @@ def group_query(q_group):
 def head_mask(qh, kg, S, B, scale, tau_num, tau_den, rows=None, normalization="R2"):
     """XA block mask of one (sequence, q-head) and its block masses.
 
-    A sequence whose length is not a whole number of blocks gets every causal
-    block (the kernel library's stated rule; XA with tau = 1, i.e. FA), and
-    P is None.  `rows` restricts scoring and selection to those block rows.
+    A sequence whose length is not a whole number of blocks has no complete
+    last block row to score, so it gets every causal block: the selection that
+    tau = 1 makes, under which XA is FA.  P is None for it.  `rows` restricts
+    scoring and selection to those block rows.
     """
     L = qh.shape[0]
     nb = -(-L // B)

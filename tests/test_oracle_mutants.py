@@ -186,3 +186,108 @@ def test_mutant_group_scores_summed(monkeypatch):
     monkeypatch.setattr(OX, "group_query", lambda q: np.asarray(q, dtype=np.float64).sum(axis=0))  # planted
     with pytest.raises(AssertionError):
         TX.test_group_query_is_the_mean_of_the_scores()
+
+
+# ---- XA pair count, tie diagnostics, block-sum masses, partial blocks ----
+
+def test_mutant_kept_pairs_diagonal_full_square(monkeypatch):
+    def square(mask, L, B):
+        nb = mask.shape[0]
+        return sum(B * B for I in range(nb) for J in np.nonzero(mask[I, : I + 1])[0])  # planted
+    monkeypatch.setattr(OX, "kept_pairs", square)
+    with pytest.raises(AssertionError):
+        TX.test_kept_pairs_hand_counts()
+
+
+def test_mutant_kept_pairs_ignores_sequence_end(monkeypatch):
+    def full_blocks(mask, L, B):
+        nb = mask.shape[0]
+        return sum(B * B if J < I else B * (B + 1) // 2                                 # planted
+                   for I in range(nb) for J in np.nonzero(mask[I, : I + 1])[0])
+    monkeypatch.setattr(OX, "kept_pairs", full_blocks)
+    with pytest.raises(AssertionError):
+        TX.test_kept_pairs_brute_force(61, 8)
+
+
+def test_mutant_tie_rule_too_broad(monkeypatch):
+    orig = OX.tie_info
+    monkeypatch.setattr(OX, "tie_info", lambda P, I, tn, td, cum_eps=1e-4, gap_rel=1e-5:
+                        orig(P, I, tn, td, cum_eps=1e-2, gap_rel=gap_rel))               # planted
+    with pytest.raises(AssertionError):
+        TX.test_tie_info_threshold_is_1e4()
+
+
+def test_mutant_tie_gap_absolute(monkeypatch):
+    orig = OX.tie_info
+
+    def absolute_gap(P_row, I, tn, td, cum_eps=1e-4, gap_rel=1e-5):
+        t = orig(P_row, I, tn, td, cum_eps=cum_eps, gap_rel=gap_rel)
+        w = OX.quantize(P_row[: I + 1])
+        order = np.lexsort((np.arange(I + 1), -w))
+        p = np.asarray(P_row[: I + 1])[order]
+        k = t["k"]
+        t["gap_tie"] = bool(k + 1 < len(p) and p[k] - p[k + 1] < 1e-4)              # planted
+        return t
+    monkeypatch.setattr(OX, "tie_info", absolute_gap)
+    with pytest.raises(AssertionError):
+        TX.test_tie_info_near_equal_masses_at_the_cut()
+
+
+def test_mutant_tie_cut_one_late(monkeypatch):
+    orig = OX.tie_info
+
+    def late(P_row, I, tn, td, cum_eps=1e-4, gap_rel=1e-5):
+        t = orig(P_row, I, tn, td, cum_eps=cum_eps, gap_rel=gap_rel)
+        t["k"] = min(t["k"] + 1, I)                                                    # planted
+        return t
+    monkeypatch.setattr(OX, "tie_info", late)
+    with pytest.raises(AssertionError):
+        TX.test_tie_info_cut_agrees_with_selector()
+
+
+def _r1_variant(strict=False, scaled=True):
+    orig = OX.block_mass
+
+    def bm(qh, kg, S, B, scale, normalization="R2", chunk_rows=1024, rows=None):
+        if normalization != "R1":
+            return orig(qh, kg, S, B, scale, normalization, chunk_rows, rows)
+        L, d = qh.shape
+        nb, r = L // B, B // S
+        Qr, Kr = OX._reduced(qh, kg, S)
+        P = np.full((nb, nb), np.nan)
+        for I in range(nb):
+            a = np.arange(I * r, (I + 1) * r)
+            s = (scale if scaled else 1.0) * (Qr[a] @ Kr[: (I + 1) * r].T)
+            bq = np.arange((I + 1) * r)
+            keep = bq[None, :] < a[:, None] if strict else bq[None, :] <= a[:, None]
+            raw = np.where(keep, s, 0.0).reshape(r, I + 1, r).sum(axis=(0, 2))
+            e = np.exp(raw - raw.max())
+            P[I, : I + 1] = e / e.sum()
+        return P
+    return bm
+
+
+def test_mutant_r1_drops_diagonal_reduced_entry(monkeypatch):
+    monkeypatch.setattr(OX, "block_mass", _r1_variant(strict=True))                    # planted
+    with pytest.raises(AssertionError):
+        TX.test_r1_block_mass_bruteforce(64, 16, 4, 5)
+
+
+def test_mutant_r1_drops_scale(monkeypatch):
+    monkeypatch.setattr(OX, "block_mass", _r1_variant(scaled=False))                   # planted
+    with pytest.raises(AssertionError):
+        TX.test_r1_block_mass_bruteforce(48, 8, 2, 3)
+
+
+def test_mutant_partial_block_diagonal_only(monkeypatch):
+    orig = OX.head_mask
+
+    def diag_only(qh, kg, S, B, scale, tn, td, rows=None, normalization="R2"):
+        L = qh.shape[0]
+        if L % B:
+            nb = -(-L // B)
+            return np.eye(nb, dtype=bool), None                                         # planted
+        return orig(qh, kg, S, B, scale, tn, td, rows=rows, normalization=normalization)
+    monkeypatch.setattr(OX, "head_mask", diag_only)
+    with pytest.raises(AssertionError):
+        TX.test_partial_last_block_is_fa(77)

@@ -184,3 +184,171 @@ def test_group_query_is_the_mean_of_the_scores():
     mg, Pg = OX.head_mask(OX.group_query(same), kg, S, B, 0.3, 9, 10)
     assert np.array_equal(m1, mg) and np.allclose(P1, Pg, rtol=1e-13, equal_nan=True)
     assert np.array_equal(OX.group_query(qg[:1]), qg[0])
+
+
+# ---- attended-pair count ------------------------------------------------
+
+def _brute_pairs(mask, L, B):
+    """(i, j) pairs counted one by one from the XA key-set definition:
+    j <= i, both inside the sequence, and block pair (i // B, j // B) selected."""
+    n = 0
+    for i in range(L):
+        for j in range(i + 1):
+            if mask[i // B, j // B]:
+                n += 1
+    return n
+
+
+@pytest.mark.parametrize("L,B", [(64, 8), (61, 8), (96, 16), (100, 16), (17, 16), (1, 4)])
+def test_kept_pairs_brute_force(L, B):
+    rng = np.random.default_rng(L * 31 + B)
+    nb = -(-L // B)
+    for trial in range(6):
+        m = np.tril(rng.random((nb, nb)) < (0.2 + 0.15 * trial))
+        if trial % 2:
+            m[np.arange(nb), np.arange(nb)] = True
+            m[:, 0] = True
+        assert OX.kept_pairs(m, L, B) == _brute_pairs(m, L, B)
+
+
+def test_kept_pairs_hand_counts():
+    B = 16
+    # Every causal block of 5 full blocks: the causal triangle of 80 tokens.
+    assert OX.kept_pairs(np.tril(np.ones((5, 5), dtype=bool)), 80, B) == 80 * 81 // 2
+    # Diagonal blocks only: B (B + 1) / 2 each, not B * B.
+    assert OX.kept_pairs(np.eye(5, dtype=bool), 80, B) == 5 * (16 * 17 // 2)
+    # Sink block of row 3 plus its diagonal: 16 * 16 + 136.
+    m = np.zeros((5, 5), dtype=bool)
+    m[3, 0] = m[3, 3] = True
+    assert OX.kept_pairs(m, 80, B) == 256 + 136
+    # A last block cut to 5 tokens: its diagonal block holds 5 * 6 / 2 pairs
+    # and its sink block 5 * 16.
+    m = np.zeros((5, 5), dtype=bool)
+    m[4, 0] = m[4, 4] = True
+    assert OX.kept_pairs(m, 69, B) == 15 + 80
+
+
+# ---- boundary-tie diagnostics -------------------------------------------
+
+def _row(sorted_masses, n_rest=6):
+    """Block row I = len + n_rest - 1 whose largest masses are `sorted_masses`
+    (in that order, at J = 1, 2, ...) and whose remaining mass is spread
+    evenly over the other n_rest blocks (J = 0 and the tail)."""
+    head = list(sorted_masses)
+    rest = (1.0 - sum(head)) / n_rest
+    assert 0 < rest < head[-1]
+    P = np.array([rest] + head + [rest] * (n_rest - 1))
+    return P, len(P) - 1
+
+
+def test_tie_info_cumulative_mass_at_tau():
+    # tau = 0.9.  The prefix 0.5 + 0.40005 reaches 0.90005: the cut's
+    # cumulative mass is 5e-5 above tau, a boundary tie.
+    P, I = _row([0.5, 0.40005])
+    t = OX.tie_info(P, I, 9, 10)
+    assert t["k"] == 1 and t["cum_tie"] and not t["gap_tie"]
+    assert abs(t["c_k"] - 0.90005) < 1e-12
+    # The prefix before the cut ends 5e-5 below tau.
+    P, I = _row([0.5, 0.39995, 0.05])
+    t = OX.tie_info(P, I, 9, 10)
+    assert t["k"] == 2 and t["cum_tie"] and abs(t["c_prev"] - 0.89995) < 1e-12
+
+
+def test_tie_info_threshold_is_1e4():
+    # 9e-5 above tau is a tie, 1.1e-4 above is not.
+    P, I = _row([0.5, 0.40009])
+    assert OX.tie_info(P, I, 9, 10)["cum_tie"]
+    P, I = _row([0.5, 0.40011])
+    t = OX.tie_info(P, I, 9, 10)
+    assert not t["cum_tie"] and not t["gap_tie"]
+
+
+def test_tie_info_near_equal_masses_at_the_cut():
+    # 0.5 + 0.35 + 0.07 = 0.92 passes tau at k = 2; the first dropped mass is
+    # 1e-6 relative below the last kept one: its order is within rounding.
+    P, I = _row([0.5, 0.35, 0.07, 0.07 * (1 - 1e-6)])
+    t = OX.tie_info(P, I, 9, 10)
+    assert t["k"] == 2 and t["gap_tie"] and not t["cum_tie"]
+    # 5e-6 apart (7e-5 relative): a real order, not a tie.
+    P, I = _row([0.5, 0.35, 0.07, 0.07 - 5e-6])
+    t = OX.tie_info(P, I, 9, 10)
+    assert t["k"] == 2 and not t["gap_tie"] and not t["cum_tie"]
+
+
+def test_tie_info_cut_agrees_with_selector():
+    # The cut position k is the selector's: k + 1 blocks of the sorted order
+    # are the top-mass prefix.
+    rng = np.random.default_rng(21)
+    for trial in range(200):
+        I = int(rng.integers(1, 40))
+        P = rng.random(I + 1) ** 6
+        P /= P.sum()
+        t = OX.tie_info(P, I, 9, 10)
+        m = OX.select_row(P, I, 9, 10)
+        order = np.lexsort((np.arange(I + 1), -OX.quantize(P)))
+        top = set(order[: t["k"] + 1].tolist())
+        assert set(np.nonzero(m)[0].tolist()) == top | {0, I}
+        assert t["c_k"] >= 0.9 - 1e-12 > t["c_prev"] - 1e-12 or t["cum_tie"]
+
+
+# ---- block-sum masses (reading R1) --------------------------------------
+
+def _brute_block_mass_r1(q, k, S, B, c):
+    """R1 from explicit loops: the raw block sum adds c <q_i, k_j> over every
+    antidiagonal entry ((i mod S) + (j mod S) = S - 1) of block (I, J) whose
+    reduced key is not after its reduced query (j // S <= i // S); each block
+    row is then softmaxed over J <= I."""
+    L = q.shape[0]
+    nb = L // B
+    raw = np.zeros((nb, nb))
+    for i in range(L):
+        for j in range(L):
+            if (i % S) + (j % S) == S - 1 and j // S <= i // S:
+                raw[i // B, j // B] += c * float(np.dot(q[i], k[j]))
+    P = np.zeros((nb, nb))
+    for I in range(nb):
+        e = np.exp(raw[I, : I + 1] - raw[I, : I + 1].max())
+        P[I, : I + 1] = e / e.sum()
+    return P
+
+
+@pytest.mark.parametrize("L,B,S,d", [(64, 16, 4, 5), (48, 8, 2, 3), (96, 32, 8, 4)])
+def test_r1_block_mass_bruteforce(L, B, S, d):
+    rng = np.random.default_rng(L + 7 * B + S)
+    q, k = rng.standard_normal((L, d)), rng.standard_normal((L, d))
+    P = OX.block_mass(q, k, S, B, 0.35, normalization="R1")
+    ref = _brute_block_mass_r1(q, k, S, B, 0.35)
+    for I in range(L // B):
+        np.testing.assert_allclose(P[I, : I + 1], ref[I, : I + 1], rtol=0, atol=1e-13)
+
+
+def test_r1_zero_query_is_uniform():
+    # q = 0: every raw block sum is 0, so each block row is uniform, 1 / (I + 1)
+    # (R2 instead gives the diagonal block about half the weight of the others).
+    L, B, S, d = 512, 64, 8, 6
+    k = np.random.default_rng(4).standard_normal((L, d))
+    P = OX.block_mass(np.zeros((L, d)), k, S, B, 0.5, normalization="R1")
+    for I in range(L // B):
+        np.testing.assert_allclose(P[I, : I + 1], 1.0 / (I + 1), rtol=0, atol=1e-15)
+
+
+# ---- sequences that are not a whole number of blocks --------------------
+
+@pytest.mark.parametrize("L", [77, 130, 5])
+def test_partial_last_block_is_fa(L):
+    # XA needs a whole number of blocks to score; such a sequence keeps every
+    # causal block (the tau = 1 selection), so its XA attention is FA.
+    from oracle import attention as OA
+    B, S, d = 16, 4, 6
+    rng = np.random.default_rng(L)
+    q, k, v = (rng.standard_normal((L, d)) for _ in range(3))
+    M, P = OX.head_mask(q, k, S, B, 0.4, 9, 10)
+    nb = -(-L // B)
+    assert P is None and M.shape == (nb, nb)
+    assert np.array_equal(M, np.tril(np.ones((nb, nb), dtype=bool)))
+    ox, lx = OA.head_attention(q, k, v, OA.MODE_XA, 0.4, block=B, xa_mask=M, chunk=32)
+    of, lf = OA.head_attention(q, k, v, OA.MODE_FA, 0.4, chunk=32)
+    np.testing.assert_array_equal(ox, of)
+    np.testing.assert_array_equal(lx, lf)
+    # Its pair count is the causal triangle of L tokens.
+    assert OX.kept_pairs(M, L, B) == L * (L + 1) // 2

@@ -2,6 +2,7 @@
 // and the host-side sparsity ratios.  See include/ea.h for the contract.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "ea_internal.h"
 
@@ -274,29 +275,98 @@ ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, co
                             workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace ea {
+
+// Host-side checks of a decode step, shared by the two decode entry points.
+static ea_status decode_check(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
+                              const void* v_dev, const int32_t* cu_seqlens_dev,
+                              const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
+                              EaDims* d, WsLayout* L, size_t* need) {
+  ea_status st = make_dims(desc, d);
+  if (st != EA_OK) return st;
+  if (d->G > 16) return EA_ERR_UNSUPPORTED;
+  if (!cu_seqlens_dev || !modes_dev) return EA_ERR_INVALID_ARG;
+  if (d->nseq > 0 && (!q_dev || !o_out_dev || !lse_out_dev)) return EA_ERR_INVALID_ARG;
+  if (d->T > 0 && (!k_dev || !v_dev)) return EA_ERR_INVALID_ARG;
+  if (misaligned(q_dev) || misaligned(k_dev) || misaligned(v_dev) || misaligned(o_out_dev) ||
+      ((uintptr_t)lse_out_dev & 3u))
+    return EA_ERR_INVALID_ARG;
+  if (d->nseq > 65535 || d->Hkv > 65535) return EA_ERR_UNSUPPORTED;
+  if (decode_waves(*d) > 0x7fffffff) return EA_ERR_UNSUPPORTED;
+  *need = ws_layout(*d, EA_OP_DECODE, L);
+  return EA_OK;
+}
+
+// Scratch of ea_hybrid_attn_decode_noalloc: the library's own device memory,
+// one copy per GPU (each at its own address), held until the process ends.
+// Host code never uses the array's name as an address: the device address
+// of the current GPU's copy comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[EA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+static std::mutex scratch_mu;
+static void* scratch_ptr[kMaxDevices];
+
+static ea_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return EA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return EA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EA_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return EA_OK;
+}
+
+}  // namespace ea
+
+extern "C" {
+
 ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
                                 const void* v_dev, const int32_t* cu_seqlens_dev,
                                 const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
                                 void* workspace_dev, size_t workspace_bytes, void* stream) {
   EaDims d;
-  ea_status st = make_dims(desc, &d);
-  if (st != EA_OK) return st;
-  if (d.G > 16) return EA_ERR_UNSUPPORTED;
-  if (!cu_seqlens_dev || !modes_dev) return EA_ERR_INVALID_ARG;
-  if (d.nseq > 0 && (!q_dev || !o_out_dev || !lse_out_dev)) return EA_ERR_INVALID_ARG;
-  if (d.T > 0 && (!k_dev || !v_dev)) return EA_ERR_INVALID_ARG;
-  if (misaligned(q_dev) || misaligned(k_dev) || misaligned(v_dev) || misaligned(o_out_dev) ||
-      ((uintptr_t)lse_out_dev & 3u))
-    return EA_ERR_INVALID_ARG;
-  if (d.nseq > 65535 || d.Hkv > 65535) return EA_ERR_UNSUPPORTED;
-  if (decode_waves(d) > 0x7fffffff) return EA_ERR_UNSUPPORTED;
   WsLayout L;
-  const size_t need = ws_layout(d, EA_OP_DECODE, &L);
+  size_t need = 0;
+  ea_status st = decode_check(desc, q_dev, k_dev, v_dev, cu_seqlens_dev, modes_dev, o_out_dev,
+                              lse_out_dev, &d, &L, &need);
+  if (st != EA_OK) return st;
   if (!workspace_dev || workspace_bytes < need) return EA_ERR_WORKSPACE;
   if (d.nseq == 0) return EA_OK;
   if (launch_decode(d, (const uint16_t*)q_dev, (const uint16_t*)k_dev, (const uint16_t*)v_dev,
                     cu_seqlens_dev, modes_dev, workspace_dev, L,
                     (uint16_t*)o_out_dev, lse_out_dev, (hipStream_t)stream) != hipSuccess)
+    return EA_ERR_HIP;
+  return EA_OK;
+}
+
+ea_status ea_hybrid_attn_decode_noalloc(const ea_attn_desc* desc, const void* q_dev,
+                                        const void* k_dev, const void* v_dev,
+                                        const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                                        void* o_out_dev, float* lse_out_dev, void* stream) {
+  EaDims d;
+  WsLayout L;
+  size_t need = 0;
+  ea_status st = decode_check(desc, q_dev, k_dev, v_dev, cu_seqlens_dev, modes_dev, o_out_dev,
+                              lse_out_dev, &d, &L, &need);
+  if (st != EA_OK) return st;
+  if (need > (size_t)EA_DECODE_NOALLOC_SCRATCH_BYTES) return EA_ERR_WORKSPACE;
+  if (d.nseq == 0) return EA_OK;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != EA_OK) return st;
+  // Nothing in the scratch has to start at zero: the plan kernel writes the
+  // split and the wave list, and the combine reads only the partials that
+  // this step's own waves wrote.
+  if (launch_decode(d, (const uint16_t*)q_dev, (const uint16_t*)k_dev, (const uint16_t*)v_dev,
+                    cu_seqlens_dev, modes_dev, ws, L, (uint16_t*)o_out_dev, lse_out_dev,
+                    (hipStream_t)stream) != hipSuccess)
     return EA_ERR_HIP;
   return EA_OK;
 }

@@ -30,8 +30,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libea.so")
 EXPORTS = (
     "ea_workspace_bytes", "ea_mask_rows", "ea_mask_words", "ea_workspace_offset",
     "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_hybrid_attn_plan", "ea_hybrid_attn_run",
-    "ea_sparsity_ratios", "ea_route_heads", "ea_hybrid_attn_decode", "ea_status_string",
+    "ea_sparsity_ratios", "ea_route_heads", "ea_hybrid_attn_decode",
+    "ea_hybrid_attn_decode_noalloc", "ea_status_string",
 )
+
+# Size of the library-owned scratch of ea_hybrid_attn_decode_noalloc.
+EA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Router weight arrays in ea_router_desc order: Task MLP (w1, b1, w2, b2),
 # Router MLP (w3, b3, w4, b4); fp32, row-major [in][out].
@@ -102,6 +106,8 @@ def lib():
     L.ea_route_heads.restype = ctypes.c_int
     L.ea_hybrid_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.ea_hybrid_attn_decode.restype = ctypes.c_int
+    L.ea_hybrid_attn_decode_noalloc.argtypes = [D, P, P, P, P, P, P, P, P]
+    L.ea_hybrid_attn_decode_noalloc.restype = ctypes.c_int
     L.ea_status_string.argtypes = [ctypes.c_int]
     L.ea_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -218,3 +224,11 @@ def ea_hybrid_attn_decode(desc, q, k, v, cu_seqlens, modes, o_out, lse_out, work
         _stream(stream))
     if st != EA_OK:
         raise EaError(st, "ea_hybrid_attn_decode")
+
+
+def ea_hybrid_attn_decode_noalloc(desc, q, k, v, cu_seqlens, modes, o_out, lse_out, stream=None):
+    st = lib().ea_hybrid_attn_decode_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(modes), _ptr(o_out),
+        _ptr(lse_out), _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_hybrid_attn_decode_noalloc")

@@ -23,7 +23,9 @@
  *   - Every pointer is owned by the caller.  "_dev" pointers are device
  *     memory on the current HIP device; "_host" pointers are host memory.
  *     The library allocates nothing, keeps no global state and is reentrant
- *     as long as concurrent calls use different workspaces.
+ *     as long as concurrent calls use different workspaces; the one exception
+ *     is ea_hybrid_attn_decode_noalloc, whose scratch is a device array the
+ *     library owns (see there).
  *   - All arguments that the host can see are checked before any launch;
  *     on failure an ea_status other than EA_OK is returned and nothing is
  *     written.  Device-side data (cu_seqlens, modes) cannot be checked
@@ -246,6 +248,32 @@ ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, con
                                 const void* v_dev, const int32_t* cu_seqlens_dev,
                                 const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
                                 void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * ea_hybrid_attn_decode without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, outputs, checks and results
+ * are those of ea_hybrid_attn_decode (the same kernels run); the step's
+ * scratch (split plan, wave list, fp32 split partials) lives instead in a
+ * device array of EA_DECODE_NOALLOC_SCRATCH_BYTES that the library owns, one
+ * per GPU, held from the first call on that GPU until the process ends.
+ * The call allocates nothing: no hipMalloc / hipFree and no allocating
+ * library routine.
+ * Limit: a step whose ea_workspace_bytes(desc, EA_OP_DECODE) exceeds
+ * EA_DECODE_NOALLOC_SCRATCH_BYTES returns EA_ERR_WORKSPACE before any launch
+ * (64 MiB holds, e.g., 8 or 16 sequences of 64K cached tokens, or 64 of 8K,
+ * at 32/8 heads and d = 128).  The first call on a GPU looks up that GPU's
+ * array (EA_ERR_HIP if that fails).
+ * Concurrency: every call on one GPU uses the same array, so calls whose
+ * device work overlaps on one GPU (different streams, or host threads
+ * without ordering) race; order them on one stream or use
+ * ea_hybrid_attn_decode with separate workspaces.
+ */
+#define EA_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+ea_status ea_hybrid_attn_decode_noalloc(const ea_attn_desc* desc, const void* q_dev,
+                                        const void* k_dev, const void* v_dev,
+                                        const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                                        void* o_out_dev, float* lse_out_dev, void* stream);
 
 /*
  * Attention Router, inference pass (English paper-reading notes, 03 Method,

@@ -330,3 +330,40 @@ def test_workspace_sizes_do_not_wrap_near_int32_max():
         # fp32 partials of splits of at least 512 keys, per (sequence, q-head)
         assert 4 * hq * (T // 4096) * 130 <= dec < 2 ** 40
         assert 0 < E.ea_workspace_bytes(d, E.EA_OP_XA_SELECT) < 2 ** 60
+
+
+def test_decode_noalloc_rejects_before_any_device_work():
+    # Every case below fails on the host, before the scratch lookup or a launch.
+    L = E.lib()
+    d = desc()
+
+    def call(dd=None, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, modes=FAKE, o=FAKE, lse=FAKE)
+        a.update(kw)
+        return L.ea_hybrid_attn_decode_noalloc(ctypes.byref(dd or d), a["q"], a["k"], a["v"],
+                                               a["cu"], a["modes"], a["o"], a["lse"], None)
+
+    bad = E.EA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "cu", "modes", "o", "lse"):
+        assert call(**{name: None}) == bad, name
+    for name in ("q", "k", "v", "o"):
+        assert call(**{name: FAKE + 2}) == bad, name
+    assert call(desc(num_q_heads=34, num_kv_heads=2)) == E.EA_ERR_UNSUPPORTED
+    assert call(desc(head_dim=96)) == E.EA_ERR_UNSUPPORTED
+    # A step whose scratch would exceed the library's array is refused:
+    # 64 sequences of 64K cached tokens need about 138 MiB of fp32 partials.
+    big = desc(num_seqs=64, total_tokens=64 * 65536, max_seqlen=65536)
+    assert E.ea_workspace_bytes(big, E.EA_OP_DECODE) > E.EA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert call(big) == E.EA_ERR_WORKSPACE
+    # The limit is the stated one: 8 sequences of 64K fit.
+    fits = desc(num_seqs=8, total_tokens=8 * 65536, max_seqlen=65536)
+    assert E.ea_workspace_bytes(fits, E.EA_OP_DECODE) <= E.EA_DECODE_NOALLOC_SCRATCH_BYTES
+    # An empty batch has nothing to do.
+    empty = desc(num_seqs=0, total_tokens=0, max_seqlen=0)
+    assert call(empty, q=None, k=None, v=None, o=None, lse=None) == E.EA_OK
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "ea.h")).read()
+    m = re.search(r"#define EA_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == E.EA_DECODE_NOALLOC_SCRATCH_BYTES

@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--decode-modes", metavar="DIGITS",
                     help="with --decode-only: one mode digit per KV head (0 FA, 1 SSA, 2 XA) "
                          "in place of the workload's, e.g. 11111111")
+    ap.add_argument("--serial-sweep", action="store_true",
+                    help="time fused vs serial dispatch over model sparsity 0.125-0.875 and "
+                         "lengths 16K-256K (Llama-3.1-8B shape, FA + SSA heads) and exit")
+    ap.add_argument("--sweep-lengths", default="16384,32768,65536,131072,262144")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -291,6 +295,65 @@ def decode_bench(cfg, mode_row, L, batch, steps, warmup):
     }
 
 
+class SerialLayer:
+    """Buffers of the serial-dispatch baseline (ea_hybrid_attn_prefill_serial)
+    for one descriptor and one mode row shared by every sequence."""
+
+    def __init__(self, desc, cu_seqlens_dev, layer_modes, device):
+        import torch
+        from hybrid_sparse_full_amd import ea as E
+        self.E = E
+        self.desc = desc
+        self.cu = cu_seqlens_dev
+        self.modes = np.ascontiguousarray(layer_modes, dtype=np.uint8)
+        T, Hq, D = desc.total_tokens, desc.num_q_heads, desc.head_dim
+        self.o = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((Hq, T), dtype=torch.float32, device=device)
+        self.ws = torch.empty(E.ea_workspace_bytes(desc, E.EA_OP_PREFILL_SERIAL), dtype=torch.uint8,
+                              device=device)
+
+    def __call__(self, q, k, v):
+        self.E.ea_hybrid_attn_prefill_serial(self.desc, q, k, v, self.cu, self.modes, self.o, self.lse,
+                                             self.ws)
+
+
+def serial_sweep(lengths, steps, warmup):
+    """Fused kernel vs serial dispatch (split, one single-mode layer per group,
+    write back) over model sparsity n/8 and sequence length, one sequence of
+    seeded N(0, 1) q, k, v generated on the device (timing only)."""
+    import torch
+    from hybrid_sparse_full_amd.layer import HybridPrefill, make_desc
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Hq, Hkv, D, B = 32, 8, 128, 128
+    rows = []
+    for L in lengths:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(L)
+        q = torch.randn((L, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((L, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((L, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        desc = make_desc(num_seqs=1, total_tokens=L, max_seqlen=L, num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=D, block=B, ssa_sink=128, ssa_window=2048)
+        cu = np.array([0, L], dtype=np.int32)
+        for n_sparse in range(1, Hkv):
+            row = np.zeros(Hkv, dtype=np.uint8)
+            row[np.random.default_rng(n_sparse).permutation(Hkv)[:n_sparse]] = 1
+            fused = HybridPrefill(desc, cu, row.reshape(1, -1), device=dev)
+            _, f_ms, _ = time_steps(lambda: fused(q, k, v), steps, warmup)
+            serial = SerialLayer(desc, fused.cu, row, dev)
+            _, s_ms, _ = time_steps(lambda: serial(q, k, v), steps, warmup)
+            rec = {"seq_len": L, "omega_msr": n_sparse / Hkv, "sparse_kv_heads": int(n_sparse),
+                   "fused_ms": round(f_ms, 4), "serial_ms": round(s_ms, 4),
+                   "speedup_fused_over_serial": round(s_ms / f_ms, 4)}
+            rows.append(rec)
+            print(json.dumps(rec), flush=True)
+            del fused, serial
+        del q, k, v
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     a = parse()
     if a.calibrate_copy:
@@ -298,6 +361,13 @@ def main():
         return
     if a.traffic_from:
         write_traffic(a.traffic_from, a.config)
+        return
+    if a.serial_sweep:
+        if a.gpus != 1:
+            raise SystemExit("the sweep runs on one GPU")
+        rows = serial_sweep([int(x) for x in a.sweep_lengths.split(",")], max(a.steps, 1), a.warmup)
+        print(json.dumps({"serial_dispatch_sweep": rows, "workload": "one sequence, 32/8 heads, d 128, "
+                          "FA + SSA (sink 128, window 2048), seeded N(0,1) on the device"}), flush=True)
         return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
@@ -367,6 +437,18 @@ def main():
         decode = decode_bench(cfg, inp["modes"][0], int(np.max(inp["seqlens"])), a.decode_batch,
                               max(a.steps, 20), a.warmup)
 
+    # Serial dispatch of the same layer (split by mode, one single-mode layer
+    # per group, write back), when every sequence shares one mode row without
+    # XA heads: the baseline the fused kernel is compared with.
+    serial = None
+    mrow = inp["modes"][0]
+    if (inp["modes"] == mrow).all() and not (mrow == 2).any():
+        sl = SerialLayer(desc, layer.cu, mrow, dev)
+        _, serial_ms, _ = time_steps(lambda: sl(q, k, v), a.steps, a.warmup)
+        serial = {"ms_per_layer": round(serial_ms, 4), "fused_ms_per_layer": round(ms, 4),
+                  "speedup_fused_over_serial": round(serial_ms / ms, 4)}
+        del sl
+
     speedup = None
     allfa_ms = None
     if not a.no_all_fa:
@@ -414,6 +496,7 @@ def main():
         "omega_msr": round(float(rat["msr"][-1]), 6),
         "omega_esr": round(float(rat["esr"][-1]), 6),
         "omega_esr_pair_weighted": round(rat["esr_pairs"], 6),
+        "serial_dispatch": serial,
         "decode": decode,
         "router": {
             "ms": round(router_ms, 4),

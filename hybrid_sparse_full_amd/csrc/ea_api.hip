@@ -85,6 +85,26 @@ size_t ws_layout(const EaDims& d, int op, WsLayout* L) {
     L->total = off;
     return off;
   }
+  if (op == EA_OP_PREFILL_SERIAL) {
+    // The inner single-mode prefills run one after the other on one stream
+    // and share a workspace sized for the whole layer (either group needs
+    // less); the split copies of q, k, v, o and lse hold both groups.
+    WsLayout inner;
+    const size_t nb = ws_layout(d, EA_OP_PREFILL, &inner);
+    std::memset(L, 0, sizeof(*L));
+    off = 0;
+    L->ser_inner = take(nb);
+    L->ser_inner_bytes = nb;
+    const size_t tok = (size_t)d.T;
+    L->ser_q = take(2 * tok * d.Hq * d.D);
+    L->ser_k = take(2 * tok * d.Hkv * d.D);
+    L->ser_v = take(2 * tok * d.Hkv * d.D);
+    L->ser_o = take(2 * tok * d.Hq * d.D);
+    L->ser_lse = take(4 * tok * d.Hq);
+    L->ser_modes = take((size_t)d.nseq * d.Hkv);
+    L->total = off;
+    return off;
+  }
   if (op == EA_OP_XA_SELECT) {
     const size_t pairs = (size_t)d.nseq * d.Hq;
     L->xa_pair_bh = take(4 * pairs);
@@ -127,7 +147,9 @@ extern "C" {
 size_t ea_workspace_bytes(const ea_attn_desc* desc, int op) {
   EaDims d;
   if (make_dims(desc, &d) != EA_OK) return 0;
-  if (op != EA_OP_XA_SELECT && op != EA_OP_PREFILL && op != EA_OP_DECODE) return 0;
+  if (op != EA_OP_XA_SELECT && op != EA_OP_PREFILL && op != EA_OP_DECODE &&
+      op != EA_OP_PREFILL_SERIAL)
+    return 0;
   WsLayout L;
   return ws_layout(d, op, &L);
 }
@@ -273,6 +295,89 @@ ea_status ea_hybrid_attn_prefill(const ea_attn_desc* desc, const void* q_dev, co
   if (st != EA_OK) return st;
   return ea_hybrid_attn_run(desc, q_dev, modes_dev, o_out_dev, lse_out_dev, workspace_dev,
                             workspace_bytes, stream);
+}
+
+ea_status ea_hybrid_attn_prefill_serial(const ea_attn_desc* desc, const void* q_dev,
+                                        const void* k_dev, const void* v_dev,
+                                        const int32_t* cu_seqlens_dev,
+                                        const uint8_t* layer_modes_host, void* o_out_dev,
+                                        float* lse_out_dev, void* workspace_dev,
+                                        size_t workspace_bytes, void* stream) {
+  EaDims d;
+  ea_status st = make_dims(desc, &d);
+  if (st != EA_OK) return st;
+  if (!cu_seqlens_dev || !layer_modes_host) return EA_ERR_INVALID_ARG;
+  if (d.T > 0 && (!q_dev || !k_dev || !v_dev || !o_out_dev || !lse_out_dev))
+    return EA_ERR_INVALID_ARG;
+  if (misaligned(q_dev) || misaligned(k_dev) || misaligned(v_dev) || misaligned(o_out_dev) ||
+      ((uintptr_t)lse_out_dev & 3u))
+    return EA_ERR_INVALID_ARG;
+  for (int g = 0; g < d.Hkv; ++g) {
+    if (layer_modes_host[g] > EA_MODE_XA) return EA_ERR_INVALID_ARG;
+    if (layer_modes_host[g] == EA_MODE_XA) return EA_ERR_UNSUPPORTED;
+  }
+  if (d.Hq > EA_SERIAL_MAX_HEADS) return EA_ERR_UNSUPPORTED;
+  WsLayout L;
+  const size_t need = ws_layout(d, EA_OP_PREFILL_SERIAL, &L);
+  if (!workspace_dev || workspace_bytes < need) return EA_ERR_WORKSPACE;
+  if (d.T == 0) return EA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)workspace_dev;
+  // 1. Split: the KV heads of each mode and their q-heads, copied into
+  //    contiguous tensors of their own (full group first).
+  HeadMap kmap[2], qmap[2];
+  for (int grp = 0; grp < 2; ++grp) {
+    kmap[grp].n = qmap[grp].n = 0;
+    const uint8_t mode = grp == 0 ? EA_MODE_FA : EA_MODE_SSA;
+    for (int g = 0; g < d.Hkv; ++g)
+      if (layer_modes_host[g] == mode) {
+        kmap[grp].idx[kmap[grp].n++] = g;
+        for (int u = 0; u < d.G; ++u) qmap[grp].idx[qmap[grp].n++] = g * d.G + u;
+      }
+  }
+  const int64_t T = d.T;
+  uint16_t* qs[2];
+  uint16_t* ks[2];
+  uint16_t* vs[2];
+  uint16_t* os[2];
+  float* ls[2];
+  uint8_t* ms[2];
+  for (int grp = 0; grp < 2; ++grp) {
+    const int64_t hq0 = grp == 0 ? 0 : qmap[0].n, hk0 = grp == 0 ? 0 : kmap[0].n;
+    qs[grp] = (uint16_t*)(w + L.ser_q) + T * hq0 * d.D;
+    ks[grp] = (uint16_t*)(w + L.ser_k) + T * hk0 * d.D;
+    vs[grp] = (uint16_t*)(w + L.ser_v) + T * hk0 * d.D;
+    os[grp] = (uint16_t*)(w + L.ser_o) + T * hq0 * d.D;
+    ls[grp] = (float*)(w + L.ser_lse) + T * hq0;
+    ms[grp] = (uint8_t*)(w + L.ser_modes) + (int64_t)d.nseq * hk0;
+  }
+  for (int grp = 0; grp < 2; ++grp) {
+    if (kmap[grp].n == 0) continue;
+    if (launch_gather_heads(d.D, (const uint16_t*)q_dev, d.Hq, qs[grp], qmap[grp], T, s) != hipSuccess ||
+        launch_gather_heads(d.D, (const uint16_t*)k_dev, d.Hkv, ks[grp], kmap[grp], T, s) != hipSuccess ||
+        launch_gather_heads(d.D, (const uint16_t*)v_dev, d.Hkv, vs[grp], kmap[grp], T, s) != hipSuccess ||
+        launch_fill_u8(ms[grp], (int64_t)d.nseq * kmap[grp].n, grp == 0 ? EA_MODE_FA : EA_MODE_SSA, s) !=
+            hipSuccess)
+      return EA_ERR_HIP;
+  }
+  // 2. One single-mode layer per group: all-FA, then all-SSA.
+  for (int grp = 0; grp < 2; ++grp) {
+    if (kmap[grp].n == 0) continue;
+    ea_attn_desc sub = *desc;
+    sub.num_kv_heads = kmap[grp].n;
+    sub.num_q_heads = qmap[grp].n;
+    st = ea_hybrid_attn_prefill(&sub, qs[grp], ks[grp], vs[grp], cu_seqlens_dev, ms[grp], nullptr,
+                                os[grp], ls[grp], w + L.ser_inner, L.ser_inner_bytes, stream);
+    if (st != EA_OK) return st;
+  }
+  // 3. Write both groups back into the layer's o and lse.
+  for (int grp = 0; grp < 2; ++grp) {
+    if (kmap[grp].n == 0) continue;
+    if (launch_scatter_heads(d.D, os[grp], ls[grp], (uint16_t*)o_out_dev, d.Hq, lse_out_dev, qmap[grp],
+                             T, s) != hipSuccess)
+      return EA_ERR_HIP;
+  }
+  return EA_OK;
 }
 
 }  // extern "C"

@@ -65,6 +65,8 @@ struct WsLayout {
   size_t kvp, unit_cost, row_cost, row_off, hist, cursor, sorted_units, tiles;
   // decode
   size_t dec_plan, dec_waves, dec_part;
+  // serial dispatch: the inner prefill's workspace, then the split copies
+  size_t ser_inner, ser_inner_bytes, ser_q, ser_k, ser_v, ser_o, ser_lse, ser_modes;
   size_t total;
 };
 
@@ -122,6 +124,18 @@ inline int64_t decode_waves(const EaDims& d) {
 hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* cu, const uint8_t* modes, void* ws, const WsLayout& L,
                          uint16_t* o, float* lse, hipStream_t st);
+// Serial dispatch: head lists (j -> head index) for the split copies.
+constexpr int EA_SERIAL_MAX_HEADS = 256;
+struct HeadMap {
+  int32_t n;
+  int32_t idx[EA_SERIAL_MAX_HEADS];
+};
+hipError_t launch_gather_heads(int D, const uint16_t* src, int32_t hs, uint16_t* dst,
+                               const HeadMap& map, int64_t T, hipStream_t st);
+hipError_t launch_scatter_heads(int D, const uint16_t* src, const float* lse_src, uint16_t* dst,
+                                int32_t hd, float* lse_dst, const HeadMap& map, int64_t T,
+                                hipStream_t st);
+hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t v, hipStream_t st);
 hipError_t launch_route(const EaDims& d, const ea_router_desc& w, const uint16_t* k,
                         const int32_t* cu, uint8_t retrieval_mode, uint8_t sparse_mode,
                         uint8_t* modes, float* logits, hipStream_t st);

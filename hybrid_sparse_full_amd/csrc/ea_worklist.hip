@@ -50,9 +50,11 @@ __device__ inline bool tile_needs_mask(const EaDims& d, int mode, int32_t I, int
   if (J >= I) return true;               // diagonal (J > I never listed)
   if (j1 >= len) return true;            // keys past the sequence end
   if (mode == EA_MODE_SSA) {
-    const bool all_sink = j1 < d.sink;
-    const bool all_window = ilast - j0 < d.window;
-    return !(all_sink || all_window);
+    // Keys before jm are sink keys; every key from jm on is kept for every
+    // query of the block iff the last query still has jm inside its window.
+    const int64_t jm = max<int64_t>(j0, d.sink);
+    if (jm > j1) return false;
+    return ilast - jm >= d.window;
   }
   return false;
 }

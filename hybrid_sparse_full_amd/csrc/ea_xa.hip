@@ -277,14 +277,20 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
   if (row >= d.nqb_max * d.Hq) return;
   const int32_t qbg = (int32_t)(row / d.Hq);
   const int h = (int)(row % d.Hq);
-  if (qbg >= m.scal[SCAL_TOTAL_QB]) return;
+  uint32_t* mrow = mask + row * d.words;
+  if (qbg >= m.scal[SCAL_TOTAL_QB]) {
+    // Rows past the last q-block of the batch (the row count is a bound
+    // from the descriptor): written as empty, like rows of non-XA heads.
+    for (int w = lane; w < d.words; w += 64) mrow[w] = 0u;
+    if (lane == 0) row_count[row] = 0;
+    return;
+  }
   uint32_t* wgt = dyn + (size_t)wv * (d.maxqb + d.words);
   uint32_t* bits = wgt + d.maxqb;
   const int32_t b = m.qb2seq[qbg];
   const int32_t I = qbg - m.qb_prefix[b];
   const int32_t len = m.len[b];
   const int mode = sane_mode(modes[(int64_t)b * d.Hkv + h / d.G]);
-  uint32_t* mrow = mask + row * d.words;
   const int32_t nI = I + 1;
   if (mode != EA_MODE_XA) {
     for (int w = lane; w < d.words; w += 64) mrow[w] = 0u;

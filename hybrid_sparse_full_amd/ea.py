@@ -23,6 +23,7 @@ EA_MODE_XA = 2
 EA_OP_XA_SELECT = 0
 EA_OP_PREFILL = 1
 EA_OP_DECODE = 2
+EA_OP_PREFILL_SERIAL = 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libea.so")
 
@@ -31,7 +32,7 @@ EXPORTS = (
     "ea_workspace_bytes", "ea_mask_rows", "ea_mask_words", "ea_workspace_offset",
     "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_hybrid_attn_plan", "ea_hybrid_attn_run",
     "ea_sparsity_ratios", "ea_route_heads", "ea_hybrid_attn_decode",
-    "ea_hybrid_attn_decode_noalloc", "ea_status_string",
+    "ea_hybrid_attn_decode_noalloc", "ea_hybrid_attn_prefill_serial", "ea_status_string",
 )
 
 # Size of the library-owned scratch of ea_hybrid_attn_decode_noalloc.
@@ -108,6 +109,8 @@ def lib():
     L.ea_hybrid_attn_decode.restype = ctypes.c_int
     L.ea_hybrid_attn_decode_noalloc.argtypes = [D, P, P, P, P, P, P, P, P]
     L.ea_hybrid_attn_decode_noalloc.restype = ctypes.c_int
+    L.ea_hybrid_attn_prefill_serial.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.ea_hybrid_attn_prefill_serial.restype = ctypes.c_int
     L.ea_status_string.argtypes = [ctypes.c_int]
     L.ea_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -194,6 +197,17 @@ def ea_hybrid_attn_run(desc, q, modes, o_out, lse_out, workspace, stream=None):
         _nbytes(workspace) if workspace is not None else 0, _stream(stream))
     if st != EA_OK:
         raise EaError(st, "ea_hybrid_attn_run")
+
+
+def ea_hybrid_attn_prefill_serial(desc, q, k, v, cu_seqlens, layer_modes_host, o_out, lse_out,
+                                  workspace, stream=None):
+    """layer_modes_host: numpy uint8 [num_kv_heads] (host memory)."""
+    st = lib().ea_hybrid_attn_prefill_serial(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(layer_modes_host),
+        _ptr(o_out), _ptr(lse_out), _ptr(workspace),
+        _nbytes(workspace) if workspace is not None else 0, _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_hybrid_attn_prefill_serial")
 
 
 def ea_sparsity_ratios(desc, cu_seqlens_host, modes_host, sparse_mode, xa_pairs_host,

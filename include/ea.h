@@ -83,6 +83,7 @@ typedef struct {
 #define EA_OP_XA_SELECT 0
 #define EA_OP_PREFILL 1
 #define EA_OP_DECODE 2
+#define EA_OP_PREFILL_SERIAL 3
 
 /*
  * Workspace bytes that `op` needs for `desc`: an upper bound computed from
@@ -120,17 +121,20 @@ int32_t ea_mask_words(const ea_attn_desc* desc);
  *           mass reaches tau * sum_J w_J, then add J = 0 and J = I.
  * Each q-head scores and selects its own mask (xa_group = 0), or every KV
  * head scores once with s^ averaged over its q-heads and all of them get that
- * mask (xa_group = 1: one reading of per-KV-head selection); XA runs on
- * sequences whose length is a multiple of B.  On an XA head of a sequence with L % B != 0,
- * every causal block is selected (XA with tau = 1, which is FA).
+ * mask (xa_group = 1: one reading of per-KV-head selection).  XA scores
+ * sequences whose length is a multiple of B; on an XA head of a sequence
+ * with L % B != 0 (no whole last block row to score) every causal block is
+ * selected, which is what tau = 1 selects and makes XA equal to FA
+ * (row_count = I + 1 on every such row).
  *
  * Inputs  q [T,Hq,d] bf16, k [T,Hkv,d] bf16, cu_seqlens_dev int32[num_seqs+1],
  *         modes_dev uint8[num_seqs * Hkv] (row-major [seq][kv head]).
- * Outputs (device; every row of every q-head is written)
+ * Outputs (device; all ea_mask_rows rows are written)
  *   mask_out_dev       uint32[ea_mask_rows][ea_mask_words]; rows of non-XA
- *                      heads are written as all-zero.
+ *                      heads, and the rows past the batch's last q-block
+ *                      (ea_mask_rows is a bound), are written as all-zero.
  *   row_count_out_dev  int32[ea_mask_rows]: selected blocks per row (0 for
- *                      non-XA heads).
+ *                      non-XA heads and for the rows past the last q-block).
  *   xa_pairs_out_dev   int64[num_seqs * Hq]: attended (i, j) pairs per
  *                      (sequence, q-head); 0 for non-XA heads.
  *   block_mass_out_dev float32[ea_mask_rows][ceil(max_seqlen / B)] or NULL:
@@ -193,6 +197,30 @@ ea_status ea_hybrid_attn_plan(const ea_attn_desc* desc, const void* k_dev, const
 ea_status ea_hybrid_attn_run(const ea_attn_desc* desc, const void* q_dev,
                              const uint8_t* modes_dev, void* o_out_dev, float* lse_out_dev,
                              void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * The same layer by serial dispatch: the baseline that the fused kernel is
+ * measured against (English paper-reading notes, 04 Deployment, Algorithm 1
+ * (a) and Figure 4; Chinese notes, 05 Deployment).  The heads are split by
+ * mode into a full group (FA) and a sparse group (SSA) with explicit copies
+ * of q, k and v, each group runs as its own single-mode layer
+ * (ea_hybrid_attn_prefill with every head in that mode), and both outputs are
+ * copied back into o_out_dev / lse_out_dev.  The result is bit-identical to
+ * ea_hybrid_attn_prefill with the same modes: the same kernels compute every
+ * row in the same order.
+ * layer_modes_host: uint8[num_kv_heads], host memory, one mode per KV head
+ *   for every sequence of the batch (the split needs the group sizes on the
+ *   host); FA or SSA (XA returns EA_ERR_UNSUPPORTED).
+ * Other arguments as for ea_hybrid_attn_prefill (no XA mask); num_q_heads
+ * <= 256.  Workspace: ea_workspace_bytes(desc, EA_OP_PREFILL_SERIAL) bytes of
+ * device memory (the split copies plus one inner prefill workspace).
+ */
+ea_status ea_hybrid_attn_prefill_serial(const ea_attn_desc* desc, const void* q_dev,
+                                        const void* k_dev, const void* v_dev,
+                                        const int32_t* cu_seqlens_dev,
+                                        const uint8_t* layer_modes_host, void* o_out_dev,
+                                        float* lse_out_dev, void* workspace_dev,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * Model and effective sparsity ratios (Eq. 4 and Eq. 5 of the Chinese

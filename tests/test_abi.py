@@ -367,3 +367,36 @@ def test_noalloc_scratch_size_matches_header():
     src = open(os.path.join(ROOT, "include", "ea.h")).read()
     m = re.search(r"#define EA_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == E.EA_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def test_serial_dispatch_rejects_before_any_device_work():
+    L = E.lib()
+    d = desc()
+    need = E.ea_workspace_bytes(d, E.EA_OP_PREFILL_SERIAL)
+    # Split copies of q, k, v, o and lse, plus one whole-layer prefill workspace.
+    T, Hq, Hkv, D = 4096, 32, 8, 128
+    assert need >= E.ea_workspace_bytes(d, E.EA_OP_PREFILL) + 2 * T * D * (2 * Hq + 2 * Hkv) + 4 * T * Hq
+    modes = np.array([0, 1, 1, 0, 1, 1, 0, 1], dtype=np.uint8)
+
+    def call(dd=None, m=modes, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, o=FAKE, lse=FAKE, ws=FAKE, n=need)
+        a.update(kw)
+        return L.ea_hybrid_attn_prefill_serial(ctypes.byref(dd or d), a["q"], a["k"], a["v"], a["cu"],
+                                               None if m is None else m.ctypes.data, a["o"], a["lse"],
+                                               a["ws"], a["n"], None)
+
+    bad = E.EA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "cu", "o", "lse"):
+        assert call(**{name: None}) == bad, name
+    assert call(m=None) == bad
+    for name in ("q", "k", "v", "o"):
+        assert call(**{name: FAKE + 8}) == bad, name
+    assert call(m=np.array([0, 1, 1, 0, 1, 1, 0, 3], dtype=np.uint8)) == bad
+    # The pages' serial baseline splits full and sliding-window heads; XA is not built for it.
+    assert call(m=np.array([0, 1, 1, 0, 2, 1, 0, 1], dtype=np.uint8)) == E.EA_ERR_UNSUPPORTED
+    assert call(ws=None) == E.EA_ERR_WORKSPACE
+    assert call(n=need - 1) == E.EA_ERR_WORKSPACE
+    assert call(desc(num_q_heads=512, num_kv_heads=8)) == E.EA_ERR_UNSUPPORTED
+    empty = desc(num_seqs=0, total_tokens=0, max_seqlen=0)
+    assert call(empty, q=None, k=None, v=None, o=None, lse=None,
+                n=E.ea_workspace_bytes(empty, E.EA_OP_PREFILL_SERIAL)) == E.EA_OK

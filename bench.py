@@ -278,7 +278,27 @@ def decode_bench(cfg, mode_row, L, batch, steps, warmup):
 
     ms, nbytes = run(modes)
     fa_ms, fa_bytes = run(np.zeros_like(modes))
-    del k, v
+
+    # The same step over the segmented cache, where SSA heads keep only their
+    # sink and window keys (filled from the packed cache above).
+    from hybrid_sparse_full_amd.layer import SegmentedDecodeCache
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).to(dev)
+    cache = SegmentedDecodeCache(desc, modes, np.full(batch, L, dtype=np.int32), device=dev)
+    cache.fill(desc, k, v, cu_dev)
+    o_c = torch.empty((batch, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse_c = torch.empty((batch, Hq), dtype=torch.float32, device=dev)
+    from hybrid_sparse_full_amd import ea as E
+    ws_c = torch.empty(E.ea_workspace_bytes(desc, E.EA_OP_DECODE), dtype=torch.uint8, device=dev)
+    _, cached_ms, _ = time_steps(lambda: cache.decode(desc, q, cu_dev, o_c, lse_c, ws_c), steps, warmup)
+    packed_cache_bytes = 2 * T * Hkv * D * 2
+    cached = {
+        "ms_per_step": round(cached_ms, 5),
+        "cache_bytes": cache.nbytes(),
+        "packed_cache_bytes": packed_cache_bytes,
+        "cache_fraction": round(cache.nbytes() / packed_cache_bytes, 4),
+        "hbm_gbs": round(nbytes / (cached_ms * 1e-3) / 1e9, 1),
+    }
+    del k, v, cache
     torch.cuda.synchronize()
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {
@@ -291,6 +311,7 @@ def decode_bench(cfg, mode_row, L, batch, steps, warmup):
         "all_fa_ms_per_step": round(fa_ms, 5),
         "all_fa_gbs": round(fa_bytes / (fa_ms * 1e-3) / 1e9, 1),
         "speedup_vs_all_fa": round(fa_ms / ms, 4),
+        "segmented_cache": cached,
         "data": "seeded N(0,1) cache on the device",
     }
 
@@ -436,6 +457,9 @@ def main():
     if a.decode_batch > 0:
         decode = decode_bench(cfg, inp["modes"][0], int(np.max(inp["seqlens"])), a.decode_batch,
                               max(a.steps, 20), a.warmup)
+        if a.decode_batch != 1:
+            decode["batch_1"] = decode_bench(cfg, inp["modes"][0], int(np.max(inp["seqlens"])), 1,
+                                             max(a.steps, 20), a.warmup)
 
     # Serial dispatch of the same layer (split by mode, one single-mode layer
     # per group, write back), when every sequence shares one mode row without

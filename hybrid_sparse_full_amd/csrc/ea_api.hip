@@ -451,6 +451,99 @@ ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, con
   return EA_OK;
 }
 
+ea_status ea_decode_cache_layout(const ea_attn_desc* desc, const uint8_t* modes_host,
+                                 const int32_t* capacity_host, int64_t* seg_off_host) {
+  EaDims d;
+  ea_status st = make_dims(desc, &d);
+  if (st != EA_OK) return st;
+  if (!seg_off_host || (d.nseq > 0 && (!modes_host || !capacity_host))) return EA_ERR_INVALID_ARG;
+  for (int b = 0; b < d.nseq; ++b) {
+    if (capacity_host[b] < 0) return EA_ERR_INVALID_ARG;
+    for (int g = 0; g < d.Hkv; ++g)
+      if (modes_host[(size_t)b * d.Hkv + g] > EA_MODE_XA) return EA_ERR_INVALID_ARG;
+  }
+  const int64_t ring = (int64_t)d.sink + d.window;
+  int64_t off = 0;
+  seg_off_host[0] = 0;
+  for (int b = 0; b < d.nseq; ++b)
+    for (int g = 0; g < d.Hkv; ++g) {
+      const int64_t cap = capacity_host[b];
+      const bool ssa = modes_host[(size_t)b * d.Hkv + g] == EA_MODE_SSA;
+      off += ssa ? (cap < ring ? cap : ring) : cap;
+      seg_off_host[(size_t)b * d.Hkv + g + 1] = off;
+    }
+  return EA_OK;
+}
+
+static ea_status cache_check(const ea_attn_desc* desc, EaDims* d, const void* a_dev, const void* b_dev,
+                             const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                             const int64_t* seg_off_dev, int64_t cache_rows, const void* kc,
+                             const void* vc) {
+  ea_status st = make_dims(desc, d);
+  if (st != EA_OK) return st;
+  if (!cu_seqlens_dev || !modes_dev || !seg_off_dev || cache_rows < 0) return EA_ERR_INVALID_ARG;
+  if (d->T > 0 && (!a_dev || !b_dev || !kc || !vc || cache_rows < 1)) return EA_ERR_INVALID_ARG;
+  if (misaligned(a_dev) || misaligned(b_dev) || misaligned(kc) || misaligned(vc)) return EA_ERR_INVALID_ARG;
+  if ((int64_t)d->nseq * d->Hkv > 65535) return EA_ERR_UNSUPPORTED;
+  return EA_OK;
+}
+
+ea_status ea_decode_cache_fill(const ea_attn_desc* desc, const void* k_dev, const void* v_dev,
+                               const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                               const int64_t* seg_off_dev, int64_t cache_rows, void* k_cache_dev,
+                               void* v_cache_dev, void* stream) {
+  EaDims d;
+  ea_status st = cache_check(desc, &d, k_dev, v_dev, cu_seqlens_dev, modes_dev, seg_off_dev, cache_rows,
+                             k_cache_dev, v_cache_dev);
+  if (st != EA_OK) return st;
+  if (d.T == 0 || d.nseq == 0) return EA_OK;
+  if (launch_cache_fill(d, (const uint16_t*)k_dev, (const uint16_t*)v_dev, cu_seqlens_dev, modes_dev,
+                        seg_off_dev, cache_rows, (uint16_t*)k_cache_dev, (uint16_t*)v_cache_dev,
+                        (hipStream_t)stream) != hipSuccess)
+    return EA_ERR_HIP;
+  return EA_OK;
+}
+
+ea_status ea_decode_cache_append(const ea_attn_desc* desc, const void* k_new_dev,
+                                 const void* v_new_dev, const int32_t* cu_seqlens_dev,
+                                 const uint8_t* modes_dev, const int64_t* seg_off_dev,
+                                 int64_t cache_rows, void* k_cache_dev, void* v_cache_dev,
+                                 void* stream) {
+  EaDims d;
+  ea_status st = cache_check(desc, &d, k_new_dev, v_new_dev, cu_seqlens_dev, modes_dev, seg_off_dev,
+                             cache_rows, k_cache_dev, v_cache_dev);
+  if (st != EA_OK) return st;
+  if (d.T == 0 || d.nseq == 0) return EA_OK;
+  if (launch_cache_append(d, (const uint16_t*)k_new_dev, (const uint16_t*)v_new_dev, cu_seqlens_dev,
+                          modes_dev, seg_off_dev, cache_rows, (uint16_t*)k_cache_dev,
+                          (uint16_t*)v_cache_dev, (hipStream_t)stream) != hipSuccess)
+    return EA_ERR_HIP;
+  return EA_OK;
+}
+
+ea_status ea_hybrid_attn_decode_cached(const ea_attn_desc* desc, const void* q_dev,
+                                       const void* k_cache_dev, const void* v_cache_dev,
+                                       const int64_t* seg_off_dev, int64_t cache_rows,
+                                       const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                                       void* o_out_dev, float* lse_out_dev, void* workspace_dev,
+                                       size_t workspace_bytes, void* stream) {
+  EaDims d;
+  WsLayout L;
+  size_t need = 0;
+  ea_status st = decode_check(desc, q_dev, k_cache_dev, v_cache_dev, cu_seqlens_dev, modes_dev,
+                              o_out_dev, lse_out_dev, &d, &L, &need);
+  if (st != EA_OK) return st;
+  if (!seg_off_dev || cache_rows < 0 || (d.T > 0 && cache_rows < 1)) return EA_ERR_INVALID_ARG;
+  if (!workspace_dev || workspace_bytes < need) return EA_ERR_WORKSPACE;
+  if (d.nseq == 0) return EA_OK;
+  if (launch_decode(d, (const uint16_t*)q_dev, (const uint16_t*)k_cache_dev,
+                    (const uint16_t*)v_cache_dev, cu_seqlens_dev, modes_dev, workspace_dev, L,
+                    (uint16_t*)o_out_dev, lse_out_dev, (hipStream_t)stream, seg_off_dev,
+                    cache_rows) != hipSuccess)
+    return EA_ERR_HIP;
+  return EA_OK;
+}
+
 ea_status ea_hybrid_attn_decode_noalloc(const ea_attn_desc* desc, const void* q_dev,
                                         const void* k_dev, const void* v_dev,
                                         const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,

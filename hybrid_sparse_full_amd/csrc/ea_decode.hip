@@ -49,9 +49,33 @@ struct DecArgs {
   float* part;         // [nseq, Hq, nsplit_max, D + 2]
   const int32_t* plan;  // null: split is fixed; else [0] split, [1] listed waves
   const int2* wlist;    // (unit, split) per listed wave, unit = (b Hkv + g) (G / GW) + wg
+  // Segmented cache (null: k / v are the packed [T, Hkv, D] cache): rows of
+  // (sequence b, KV head g) are [seg[b Hkv + g], seg[b Hkv + g + 1]) of a
+  // head-major [cache_rows, D] pool; an SSA segment is a ring of its sink and
+  // window keys (key j >= sink in slot sink + (j - sink) mod window).
+  const int64_t* seg;
+  int64_t cache_rows;
   int32_t nseq, Hq, Hkv, G, T, maxL, sink, window, split, nsplit_max;
   float c2;            // softmax scale * log2(e)
 };
+
+// Ring slot of key j >= sink of an SSA segment.
+__device__ inline int64_t ring_slot(int64_t j, int32_t sink, int32_t window) {
+  return (int64_t)sink + (j - sink) % window;
+}
+
+// Rows [lo, lo + cap) of unit i = b Hkv + g, clamped into the pool whatever
+// the segment table holds; `last` is the last row a read may use (inside the
+// segment, or a pool row if the segment is empty).
+__device__ inline void seg_bounds(const DecArgs& a, int64_t i, int64_t* lo, int64_t* cap,
+                                  int64_t* last) {
+  const int64_t r = a.cache_rows;
+  const int64_t s0 = min(max(a.seg[i], (int64_t)0), r);
+  const int64_t s1 = min(max(a.seg[i + 1], s0), r);
+  *lo = s0;
+  *cap = s1 - s0;
+  *last = s1 > s0 ? s1 - 1 : min(s0, r - 1);
+}
 
 // Kept keys of the decoded query (index L - 1) of a sequence of cached length L.
 __device__ inline int32_t dec_kept(int mode, int32_t L, int32_t sink, int32_t window) {
@@ -170,7 +194,7 @@ __global__ __launch_bounds__(1024) void k_decode_plan(DecArgs a, int32_t s_min, 
   }
 }
 
-template <int D, int GW>
+template <int D, int GW, bool SEG>
 __global__ __launch_bounds__(256) void k_decode(DecArgs a) {
   constexpr int LPK = D / 8;          // lanes per key row
   constexpr int KPI = 64 / LPK;       // keys per wave iteration
@@ -218,14 +242,36 @@ __global__ __launch_bounds__(256) void k_decode(DecArgs a) {
     qw[hh][0] = t.x; qw[hh][1] = t.y; qw[hh][2] = t.z; qw[hh][3] = t.w;
   }
 
+  // Segmented cache: this unit's rows, and for an SSA ring the slot of its
+  // first window key (the window keys follow in slot order, wrapping once).
+  int64_t seg_lo = 0, seg_last = 0, wslot0 = 0, ring_end = 0;
+  int32_t head = 0;
+  if (SEG) {
+    int64_t seg_cap;
+    seg_bounds(a, (int64_t)b * a.Hkv + g, &seg_lo, &seg_cap, &seg_last);
+    head = min(a.sink, L);
+    const int32_t jw0 = max(head, L - a.window);
+    wslot0 = jw0 >= a.sink ? ring_slot(jw0, a.sink, a.window) : jw0;
+    ring_end = (int64_t)a.sink + a.window;
+  }
   uint4 kr[DEC_NB][DEC_BI], vr[DEC_NB][DEC_BI];
   auto load_block = [&](int blk, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int i = 0; i < DEC_BI; ++i) {
       const int32_t p = min(p0 + (blk * DEC_BI + i) * KPI + grp, p1 - 1);
-      const int32_t j = dec_key(mode, p, L, a.sink, a.window);
-      const size_t off = ((size_t)(s0 + j) * a.Hkv + g) * D + 8 * pc;
+      size_t off;
+      if (SEG) {
+        int64_t r = p;
+        if (mode == EA_MODE_SSA && p >= head) {
+          r = wslot0 + (p - head);
+          if (r >= ring_end) r -= a.window;
+        }
+        off = (size_t)min(seg_lo + r, seg_last) * D + 8 * pc;
+      } else {
+        const int32_t j = dec_key(mode, p, L, a.sink, a.window);
+        off = ((size_t)(s0 + j) * a.Hkv + g) * D + 8 * pc;
+      }
       kr[sl][i] = *(const uint4*)(a.k + off);
       vr[sl][i] = *(const uint4*)(a.v + off);
     }
@@ -380,10 +426,110 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecArgs a, uint16_t* out
   }
 }
 
+// ------------------------------------------------------- segmented cache
+// Fill: every kept key of every (sequence, KV head) of a packed [T, Hkv, D]
+// k / v (e.g. the prefill's) into its segment row; one block covers RPB key
+// positions of one unit, 16 bytes per thread.
+template <int D>
+__global__ __launch_bounds__(256) void k_cache_fill(DecArgs a, const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v,
+                                                    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
+  constexpr int CPR = D / 8, RPB = 256 / CPR;
+  const int64_t unit = blockIdx.y;
+  const int b = (int)(unit / a.Hkv), g = (int)(unit % a.Hkv);
+  int32_t s0, L;
+  seq_bounds(a, b, &s0, &L);
+  int mode = sane_mode(a.modes[unit]);
+  if (mode == EA_MODE_XA) mode = EA_MODE_FA;
+  const int32_t n = dec_kept(mode, L, a.sink, a.window);
+  int64_t lo, cap, last;
+  seg_bounds(a, unit, &lo, &cap, &last);
+  const int32_t p = (int32_t)blockIdx.x * RPB + (int32_t)(threadIdx.x / CPR);
+  const int c = threadIdx.x % CPR;
+  if (p >= n) return;
+  const int32_t j = dec_key(mode, p, L, a.sink, a.window);
+  const int64_t r = (mode == EA_MODE_SSA && j >= a.sink) ? ring_slot(j, a.sink, a.window) : j;
+  if (r >= cap) return;
+  const size_t src = ((size_t)(s0 + j) * a.Hkv + g) * D + 8 * c;
+  const size_t dst = (size_t)(lo + r) * D + 8 * c;
+  *(uint4*)(kc + dst) = *(const uint4*)(k + src);
+  *(uint4*)(vc + dst) = *(const uint4*)(v + src);
+}
+
+// Append: the newest token (index L - 1 of each sequence, L from
+// cu_seqlens) of every KV head, from k_new / v_new [nseq, Hkv, D], into its
+// row or ring slot.
+template <int D>
+__global__ __launch_bounds__(256) void k_cache_append(DecArgs a, const uint16_t* __restrict__ kn,
+                                                      const uint16_t* __restrict__ vn,
+                                                      uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
+  constexpr int CPR = D / 8, UPB = 256 / CPR;
+  const int64_t unit = (int64_t)blockIdx.x * UPB + threadIdx.x / CPR;
+  const int c = threadIdx.x % CPR;
+  if (unit >= (int64_t)a.nseq * a.Hkv) return;
+  const int b = (int)(unit / a.Hkv);
+  int32_t s0, L;
+  seq_bounds(a, b, &s0, &L);
+  if (L <= 0) return;
+  const int mode = sane_mode(a.modes[unit]);
+  const int64_t j = L - 1;
+  const int64_t r = (mode == EA_MODE_SSA && j >= a.sink) ? ring_slot(j, a.sink, a.window) : j;
+  int64_t lo, cap, last;
+  seg_bounds(a, unit, &lo, &cap, &last);
+  if (r >= cap) return;
+  const size_t dst = (size_t)(lo + r) * D + 8 * c;
+  const size_t src = (size_t)unit * D + 8 * c;
+  *(uint4*)(kc + dst) = *(const uint4*)(kn + src);
+  *(uint4*)(vc + dst) = *(const uint4*)(vn + src);
+}
+
+static DecArgs cache_args(const EaDims& d, const int32_t* cu, const uint8_t* modes, const int64_t* seg,
+                          int64_t cache_rows) {
+  DecArgs a = {};
+  a.cu = cu;
+  a.modes = modes;
+  a.seg = seg;
+  a.cache_rows = cache_rows;
+  a.nseq = d.nseq;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.T = d.T;
+  a.maxL = d.maxL;
+  a.sink = d.sink;
+  a.window = d.window;
+  return a;
+}
+
+hipError_t launch_cache_fill(const EaDims& d, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+                             const uint8_t* modes, const int64_t* seg, int64_t cache_rows,
+                             uint16_t* kc, uint16_t* vc, hipStream_t st) {
+  const DecArgs a = cache_args(d, cu, modes, seg, cache_rows);
+  const int rpb = 256 / (d.D / 8);
+  const dim3 grid((unsigned)cdiv(d.maxL, rpb), (unsigned)((int64_t)d.nseq * d.Hkv));
+  if (d.D == 128) hipLaunchKernelGGL(k_cache_fill<128>, grid, dim3(256), 0, st, a, k, v, kc, vc);
+  else hipLaunchKernelGGL(k_cache_fill<64>, grid, dim3(256), 0, st, a, k, v, kc, vc);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_append(const EaDims& d, const uint16_t* kn, const uint16_t* vn, const int32_t* cu,
+                               const uint8_t* modes, const int64_t* seg, int64_t cache_rows,
+                               uint16_t* kc, uint16_t* vc, hipStream_t st) {
+  const DecArgs a = cache_args(d, cu, modes, seg, cache_rows);
+  const int upb = 256 / (d.D / 8);
+  const dim3 grid((unsigned)(((int64_t)d.nseq * d.Hkv + upb - 1) / upb));
+  if (d.D == 128) hipLaunchKernelGGL(k_cache_append<128>, grid, dim3(256), 0, st, a, kn, vn, kc, vc);
+  else hipLaunchKernelGGL(k_cache_append<64>, grid, dim3(256), 0, st, a, kn, vn, kc, vc);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* cu, const uint8_t* modes, void* ws, const WsLayout& L,
-                         uint16_t* o, float* lse, hipStream_t st) {
-  DecArgs a;
+                         uint16_t* o, float* lse, hipStream_t st, const int64_t* seg,
+                         int64_t cache_rows) {
+  DecArgs a = {};
+  a.seg = seg;
+  a.cache_rows = cache_rows;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -417,10 +563,21 @@ hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, 
     const int64_t waves = decode_waves(d);
     const dim3 grid((unsigned)((waves + 3) / 4));
     void (*kern)(DecArgs) = nullptr;
-    if (d.D == 128)
-      kern = gw == 8 ? k_decode<128, 8> : gw == 4 ? k_decode<128, 4> : gw == 2 ? k_decode<128, 2> : k_decode<128, 1>;
-    else
-      kern = gw == 8 ? k_decode<64, 8> : gw == 4 ? k_decode<64, 4> : gw == 2 ? k_decode<64, 2> : k_decode<64, 1>;
+    if (seg) {
+      if (d.D == 128)
+        kern = gw == 8 ? k_decode<128, 8, true> : gw == 4 ? k_decode<128, 4, true>
+             : gw == 2 ? k_decode<128, 2, true> : k_decode<128, 1, true>;
+      else
+        kern = gw == 8 ? k_decode<64, 8, true> : gw == 4 ? k_decode<64, 4, true>
+             : gw == 2 ? k_decode<64, 2, true> : k_decode<64, 1, true>;
+    } else {
+      if (d.D == 128)
+        kern = gw == 8 ? k_decode<128, 8, false> : gw == 4 ? k_decode<128, 4, false>
+             : gw == 2 ? k_decode<128, 2, false> : k_decode<128, 1, false>;
+      else
+        kern = gw == 8 ? k_decode<64, 8, false> : gw == 4 ? k_decode<64, 4, false>
+             : gw == 2 ? k_decode<64, 2, false> : k_decode<64, 1, false>;
+    }
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
   }
   const dim3 cgrid((unsigned)d.Hq, (unsigned)d.nseq);

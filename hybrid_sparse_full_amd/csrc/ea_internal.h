@@ -121,9 +121,18 @@ inline int64_t decode_waves(const EaDims& d) {
   const double w = (double)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_splits(d);
   return w >= 4.6e18 ? ((int64_t)1 << 62) : (int64_t)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_splits(d);
 }
+// seg == nullptr: k / v are the packed [T, Hkv, D] cache; else the
+// segmented head-major cache of cache_rows rows (see ea_decode_cache_layout).
 hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* cu, const uint8_t* modes, void* ws, const WsLayout& L,
-                         uint16_t* o, float* lse, hipStream_t st);
+                         uint16_t* o, float* lse, hipStream_t st, const int64_t* seg = nullptr,
+                         int64_t cache_rows = 0);
+hipError_t launch_cache_fill(const EaDims& d, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+                             const uint8_t* modes, const int64_t* seg, int64_t cache_rows,
+                             uint16_t* kc, uint16_t* vc, hipStream_t st);
+hipError_t launch_cache_append(const EaDims& d, const uint16_t* kn, const uint16_t* vn, const int32_t* cu,
+                               const uint8_t* modes, const int64_t* seg, int64_t cache_rows,
+                               uint16_t* kc, uint16_t* vc, hipStream_t st);
 // Serial dispatch: head lists (j -> head index) for the split copies.
 constexpr int EA_SERIAL_MAX_HEADS = 256;
 struct HeadMap {

@@ -32,7 +32,9 @@ EXPORTS = (
     "ea_workspace_bytes", "ea_mask_rows", "ea_mask_words", "ea_workspace_offset",
     "ea_xa_block_select", "ea_hybrid_attn_prefill", "ea_hybrid_attn_plan", "ea_hybrid_attn_run",
     "ea_sparsity_ratios", "ea_route_heads", "ea_hybrid_attn_decode",
-    "ea_hybrid_attn_decode_noalloc", "ea_hybrid_attn_prefill_serial", "ea_status_string",
+    "ea_hybrid_attn_decode_noalloc", "ea_hybrid_attn_prefill_serial", "ea_decode_cache_layout",
+    "ea_decode_cache_fill", "ea_decode_cache_append", "ea_hybrid_attn_decode_cached",
+    "ea_status_string",
 )
 
 # Size of the library-owned scratch of ea_hybrid_attn_decode_noalloc.
@@ -111,6 +113,15 @@ def lib():
     L.ea_hybrid_attn_decode_noalloc.restype = ctypes.c_int
     L.ea_hybrid_attn_prefill_serial.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.ea_hybrid_attn_prefill_serial.restype = ctypes.c_int
+    L.ea_decode_cache_layout.argtypes = [D, P, P, P]
+    L.ea_decode_cache_layout.restype = ctypes.c_int
+    L.ea_decode_cache_fill.argtypes = [D, P, P, P, P, P, ctypes.c_int64, P, P, P]
+    L.ea_decode_cache_fill.restype = ctypes.c_int
+    L.ea_decode_cache_append.argtypes = [D, P, P, P, P, P, ctypes.c_int64, P, P, P]
+    L.ea_decode_cache_append.restype = ctypes.c_int
+    L.ea_hybrid_attn_decode_cached.argtypes = [D, P, P, P, P, ctypes.c_int64, P, P, P, P, P,
+                                               ctypes.c_size_t, P]
+    L.ea_hybrid_attn_decode_cached.restype = ctypes.c_int
     L.ea_status_string.argtypes = [ctypes.c_int]
     L.ea_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -246,3 +257,40 @@ def ea_hybrid_attn_decode_noalloc(desc, q, k, v, cu_seqlens, modes, o_out, lse_o
         _ptr(lse_out), _stream(stream))
     if st != EA_OK:
         raise EaError(st, "ea_hybrid_attn_decode_noalloc")
+
+
+def ea_decode_cache_layout(desc, modes_host, capacity_host, seg_off_out):
+    """Host arrays: modes uint8 [num_seqs*Hkv], capacity int32 [num_seqs],
+    seg_off_out int64 [num_seqs*Hkv + 1] (written)."""
+    st = lib().ea_decode_cache_layout(ctypes.byref(desc), _ptr(modes_host), _ptr(capacity_host),
+                                      _ptr(seg_off_out))
+    if st != EA_OK:
+        raise EaError(st, "ea_decode_cache_layout")
+
+
+def ea_decode_cache_fill(desc, k, v, cu_seqlens, modes, seg_off, cache_rows, k_cache, v_cache,
+                         stream=None):
+    st = lib().ea_decode_cache_fill(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(modes),
+                                    _ptr(seg_off), int(cache_rows), _ptr(k_cache), _ptr(v_cache),
+                                    _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_decode_cache_fill")
+
+
+def ea_decode_cache_append(desc, k_new, v_new, cu_seqlens, modes, seg_off, cache_rows, k_cache,
+                           v_cache, stream=None):
+    st = lib().ea_decode_cache_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens),
+                                      _ptr(modes), _ptr(seg_off), int(cache_rows), _ptr(k_cache),
+                                      _ptr(v_cache), _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_decode_cache_append")
+
+
+def ea_hybrid_attn_decode_cached(desc, q, k_cache, v_cache, seg_off, cache_rows, cu_seqlens, modes,
+                                 o_out, lse_out, workspace, stream=None):
+    st = lib().ea_hybrid_attn_decode_cached(
+        ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seg_off), int(cache_rows),
+        _ptr(cu_seqlens), _ptr(modes), _ptr(o_out), _ptr(lse_out), _ptr(workspace),
+        _nbytes(workspace) if workspace is not None else 0, _stream(stream))
+    if st != EA_OK:
+        raise EaError(st, "ea_hybrid_attn_decode_cached")

@@ -177,3 +177,44 @@ def desc_for(cfg, seqlens):
                      ssa_sink=cfg.ssa_sink, ssa_window=cfg.ssa_window, xa_stride=cfg.xa_stride,
                      xa_tau=(cfg.tau_num, cfg.tau_den), xa_group=cfg.xa_group,
                      xa_norm=cfg.xa_norm)
+
+
+class SegmentedDecodeCache:
+    """Decode cache in which SSA heads keep only their sink and window keys
+    (ea_decode_cache_layout / _fill / _append, ea_hybrid_attn_decode_cached).
+
+    `capacity` (host, int32 [num_seqs]) is the length each sequence may reach;
+    `modes` (host, [num_seqs, Hkv]) are the routing decisions the layout is
+    built for.  The pools are [rows, d] bf16 for k and for v.
+    """
+
+    def __init__(self, desc, modes, capacity, device="cuda"):
+        self.device = torch.device(device)
+        self.desc = desc
+        self.modes_host = np.ascontiguousarray(modes, dtype=np.uint8).reshape(-1)
+        self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
+        self.seg_host = np.zeros(self.modes_host.size + 1, dtype=np.int64)
+        E.ea_decode_cache_layout(desc, self.modes_host, self.capacity, self.seg_host)
+        self.rows = int(self.seg_host[-1])
+        self.seg = torch.from_numpy(self.seg_host).to(self.device)
+        self.modes = torch.from_numpy(self.modes_host).to(self.device)
+        D = desc.head_dim
+        self.k = torch.zeros((max(self.rows, 1), D), dtype=torch.bfloat16, device=self.device)
+        self.v = torch.zeros((max(self.rows, 1), D), dtype=torch.bfloat16, device=self.device)
+
+    def nbytes(self):
+        return 2 * self.rows * self.desc.head_dim * 2
+
+    def fill(self, desc, k, v, cu_seqlens_dev, stream=None):
+        """From a packed [T, Hkv, d] k / v described by desc / cu_seqlens."""
+        E.ea_decode_cache_fill(desc, k, v, cu_seqlens_dev, self.modes, self.seg, self.rows, self.k, self.v,
+                               stream)
+
+    def append(self, desc, k_new, v_new, cu_seqlens_dev, stream=None):
+        """One token per sequence; desc / cu_seqlens give the lengths after it."""
+        E.ea_decode_cache_append(desc, k_new, v_new, cu_seqlens_dev, self.modes, self.seg, self.rows,
+                                 self.k, self.v, stream)
+
+    def decode(self, desc, q, cu_seqlens_dev, o_out, lse_out, workspace, stream=None):
+        E.ea_hybrid_attn_decode_cached(desc, q, self.k, self.v, self.seg, self.rows, cu_seqlens_dev,
+                                       self.modes, o_out, lse_out, workspace, stream)

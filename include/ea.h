@@ -278,6 +278,80 @@ ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, con
                                 void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode over a cache in which SSA heads keep only their sink and window
+ * keys.  Routing is decided once per request and reused for every generated
+ * token (English paper-reading notes, 08 Commentary, the authors' stated
+ * limits, item 3), and an SSA head attends only its first ssa_sink keys and
+ * its last ssa_window keys (glossary: attention sink plus sliding window), so
+ * its older keys are never read again and need no storage.
+ *
+ * Layout: a head-major pool of cache_rows rows of head_dim bf16 for k and
+ * one for v.  (Sequence b, KV head g) owns rows [seg_off[u], seg_off[u + 1])
+ * of both pools, u = b * Hkv + g.  An FA or XA segment stores key j in row
+ * j.  An SSA segment is a ring of ssa_sink + ssa_window rows: key j < sink in
+ * row j, key j >= sink in row sink + (j - sink) mod ssa_window, so it holds
+ * exactly the keys a decode step of that head reads.
+ * The modes, sink and window used to build the layout must be the ones the
+ * cache is filled and read with (the library cannot check that).  Device
+ * data is sanitised as elsewhere: segment bounds are clamped into the pool,
+ * writes past a segment's end are dropped and reads clamped to its rows, so
+ * no table content makes a kernel touch memory outside the pools.
+ */
+
+/*
+ * Host: segment offsets for capacity_host[b] tokens per sequence (the length
+ * the sequence may reach).  FA / XA segments get capacity rows, SSA segments
+ * min(capacity, ssa_sink + ssa_window).  modes_host uint8[num_seqs * Hkv],
+ * capacity_host int32[num_seqs] (>= 0), seg_off_host int64[num_seqs * Hkv +
+ * 1] written (seg_off_host[num_seqs * Hkv] is the pool's row count).
+ * Synchronous; EA_ERR_INVALID_ARG on a null pointer, a mode > 2 or a negative
+ * capacity.
+ */
+ea_status ea_decode_cache_layout(const ea_attn_desc* desc, const uint8_t* modes_host,
+                                 const int32_t* capacity_host, int64_t* seg_off_host);
+
+/*
+ * Fill the segmented cache from a packed cache k_dev / v_dev [T, Hkv, d]
+ * (e.g. the keys and values of a prefill): for every (sequence, KV head), the
+ * keys its mode keeps for decoding the sequence's last token (desc and
+ * cu_seqlens_dev describe the packed cache).  k_cache_dev / v_cache_dev
+ * [cache_rows, d] bf16, seg_off_dev int64[num_seqs * Hkv + 1] (device copies
+ * of the layout), modes_dev uint8[num_seqs * Hkv].  num_seqs * Hkv <= 65535.
+ * Asynchronous on `stream`.
+ */
+ea_status ea_decode_cache_fill(const ea_attn_desc* desc, const void* k_dev, const void* v_dev,
+                               const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                               const int64_t* seg_off_dev, int64_t cache_rows, void* k_cache_dev,
+                               void* v_cache_dev, void* stream);
+
+/*
+ * Append one token per sequence: k_new_dev / v_new_dev [num_seqs, Hkv, d]
+ * are written as key L_b - 1 of each segment, where cu_seqlens_dev gives the
+ * lengths L_b after the append (an empty sequence appends nothing).  An SSA
+ * ring overwrites the slot of the key that just left the window.
+ */
+ea_status ea_decode_cache_append(const ea_attn_desc* desc, const void* k_new_dev,
+                                 const void* v_new_dev, const int32_t* cu_seqlens_dev,
+                                 const uint8_t* modes_dev, const int64_t* seg_off_dev,
+                                 int64_t cache_rows, void* k_cache_dev, void* v_cache_dev,
+                                 void* stream);
+
+/*
+ * One decode step over the segmented cache: the same step, split plan and
+ * key order as ea_hybrid_attn_decode over the packed cache that holds the
+ * same keys, so the outputs are bit-identical.  cu_seqlens_dev gives the
+ * cached lengths L_b (desc.total_tokens = their sum; the current token is
+ * cached); q, o, lse, modes, workspace (EA_OP_DECODE) and limits as for
+ * ea_hybrid_attn_decode.
+ */
+ea_status ea_hybrid_attn_decode_cached(const ea_attn_desc* desc, const void* q_dev,
+                                       const void* k_cache_dev, const void* v_cache_dev,
+                                       const int64_t* seg_off_dev, int64_t cache_rows,
+                                       const int32_t* cu_seqlens_dev, const uint8_t* modes_dev,
+                                       void* o_out_dev, float* lse_out_dev, void* workspace_dev,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * ea_hybrid_attn_decode without a workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, outputs, checks and results

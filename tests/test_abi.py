@@ -400,3 +400,48 @@ def test_serial_dispatch_rejects_before_any_device_work():
     empty = desc(num_seqs=0, total_tokens=0, max_seqlen=0)
     assert call(empty, q=None, k=None, v=None, o=None, lse=None,
                 n=E.ea_workspace_bytes(empty, E.EA_OP_PREFILL_SERIAL)) == E.EA_OK
+
+
+def test_decode_cache_layout_rows():
+    # FA and XA segments hold the capacity; SSA segments sink + window rows at most.
+    d = desc(num_seqs=3, total_tokens=3 * 1000, max_seqlen=1000, num_kv_heads=2, num_q_heads=4,
+             ssa_sink=5, ssa_window=20)
+    modes = np.array([0, 1, 1, 2, 1, 1], dtype=np.uint8)
+    cap = np.array([1000, 7, 0], dtype=np.int32)
+    seg = np.zeros(7, dtype=np.int64)
+    E.ea_decode_cache_layout(d, modes, cap, seg)
+    assert seg.tolist() == [0, 1000, 1025, 1032, 1039, 1039, 1039]
+    with pytest.raises(E.EaError):
+        E.ea_decode_cache_layout(d, modes, np.array([1, -1, 0], dtype=np.int32), seg)
+    with pytest.raises(E.EaError):
+        E.ea_decode_cache_layout(d, np.array([0, 1, 3, 0, 0, 0], dtype=np.uint8), cap, seg)
+
+
+def test_decode_cache_calls_reject_before_any_device_work():
+    L = E.lib()
+    d = desc()
+    bad = E.EA_ERR_INVALID_ARG
+    for fn in (L.ea_decode_cache_fill, L.ea_decode_cache_append):
+        def call(**kw):
+            a = dict(k=FAKE, v=FAKE, cu=FAKE, modes=FAKE, seg=FAKE, rows=100, kc=FAKE, vc=FAKE)
+            a.update(kw)
+            return fn(ctypes.byref(d), a["k"], a["v"], a["cu"], a["modes"], a["seg"], a["rows"], a["kc"],
+                      a["vc"], None)
+        for name in ("k", "v", "cu", "modes", "seg", "kc", "vc"):
+            assert call(**{name: None}) == bad, name
+        assert call(rows=0) == bad and call(rows=-1) == bad
+        assert call(kc=FAKE + 4) == bad
+        assert fn(ctypes.byref(desc(num_seqs=9000, total_tokens=9000, max_seqlen=1)), FAKE, FAKE, FAKE,
+                  FAKE, FAKE, 100, FAKE, FAKE, None) == E.EA_ERR_UNSUPPORTED
+    need = E.ea_workspace_bytes(d, E.EA_OP_DECODE)
+
+    def dec(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, seg=FAKE, rows=100, cu=FAKE, modes=FAKE, o=FAKE, lse=FAKE,
+                 ws=FAKE, n=need)
+        a.update(kw)
+        return L.ea_hybrid_attn_decode_cached(ctypes.byref(d), a["q"], a["kc"], a["vc"], a["seg"], a["rows"],
+                                              a["cu"], a["modes"], a["o"], a["lse"], a["ws"], a["n"], None)
+    for name in ("q", "kc", "vc", "seg", "cu", "modes", "o", "lse"):
+        assert dec(**{name: None}) == bad, name
+    assert dec(rows=0) == bad
+    assert dec(n=need - 1) == E.EA_ERR_WORKSPACE

@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-fa", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--oracle-timing", metavar="NAMES",
+                    help="comma-separated workloads: time the whole fp64 oracle layer (FA / SSA heads) "
+                         "with one thread and with the host's threads, then exit (no GPU needed)")
     ap.add_argument("--decode-batch", type=int, default=8,
                     help="sequences of the decode measurement (0 skips it)")
     ap.add_argument("--decode-only", action="store_true",
@@ -192,53 +195,107 @@ def time_steps(fn, steps, warmup):
     return wall * 1e3, float(np.mean(per)), per
 
 
-def cpu_baseline(inp, seconds):
-    """The fp64 oracle, as it stands, on a bounded sample of query rows."""
+def _oracle_head_rows(inp, heads, threads, rows_per_task=1024):
+    """The fp64 oracle (oracle.attention.head_attention, as it stands) over
+    every row of the listed (b, h) FA / SSA heads, the rows of each head split
+    into ranges run by `threads` host threads (numpy releases the GIL in its
+    products and elementwise loops; BLAS single-threaded in each task)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     from oracle import attention as OA
     from synth import bf16_bits_to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
+    cfg = inp["cfg"]
+    cu = inp["cu_seqlens"]
+    G = cfg.gqa
+    tasks = []
+    for (b, h) in heads:
+        g = h // G
+        L = int(cu[b + 1] - cu[b])
+        qh = bf16_bits_to_f64(inp["q"][cu[b]:cu[b + 1], h])
+        kh = bf16_bits_to_f64(inp["k"][cu[b]:cu[b + 1], g])
+        vh = bf16_bits_to_f64(inp["v"][cu[b]:cu[b + 1], g])
+        mode = int(inp["modes"][b, g])
+        for r0 in range(0, L, rows_per_task):
+            tasks.append((qh, kh, vh, mode, r0, min(L, r0 + rows_per_task)))
+    tasks.sort(key=lambda t: -t[5])
+
+    def run(t):
+        qh, kh, vh, mode, r0, r1 = t
+        return OA.head_attention(qh, kh, vh, mode, cfg.softmax_scale, sink=cfg.ssa_sink,
+                                 window=cfg.ssa_window, block=cfg.block, chunk=256, row_range=(r0, r1))
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        if threads == 1:
+            for t in tasks:
+                run(t)
+        else:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(run, tasks))
+
+
+def _head_pairs(cfg, L, mode):
+    """Attended (i, j) pairs of one FA / SSA q-head of a sequence of length L."""
+    if mode == 0:
+        return L * (L + 1) // 2
+    i = np.arange(L, dtype=np.int64)
+    lo = np.maximum(i - cfg.ssa_window + 1, 0)
+    return int((np.minimum(i + 1, cfg.ssa_sink) + np.maximum(0, i - np.maximum(lo, cfg.ssa_sink) + 1)).sum())
+
+
+def cpu_baseline(inp, seconds, threads=None):
+    """The fp64 oracle, as it stands, on whole q-heads of the workload: FA and
+    SSA heads in turn (XA heads need the oracle's masks first and are left
+    out), until `seconds` of wall time have passed (at least one head)."""
     cfg = inp["cfg"]
     G = cfg.gqa
-    rng = np.random.default_rng(123)
-    cu = inp["cu_seqlens"]
+    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    cand = [(b, h) for b in range(len(inp["seqlens"])) for h in range(cfg.num_q_heads)
+            if int(inp["modes"][b, h // G]) in (0, 1) and inp["seqlens"][b] > 0]
+    # FA and SSA heads alternate, so a short sample holds both.
+    fa = [x for x in cand if int(inp["modes"][x[0], x[1] // G]) == 0]
+    ssa = [x for x in cand if int(inp["modes"][x[0], x[1] // G]) == 1]
+    order = [x for pair in zip(fa, ssa) for x in pair] + fa[len(ssa):] + ssa[len(fa):]
     flops = 0.0
-    rows = 0
-    cache = {}
+    done = []
     t0 = time.perf_counter()
-    t_work = 0.0
-    while t_work < seconds:
-        b = int(rng.integers(len(inp["seqlens"])))
+    for (b, h) in order:
+        _oracle_head_rows(inp, [(b, h)], threads)
         L = int(inp["seqlens"][b])
-        h = int(rng.integers(cfg.num_q_heads))
-        g = h // G
-        mode = int(inp["modes"][b, g])
-        if mode == 2:
-            continue
-        if (b, g) not in cache:
-            cache[(b, g)] = (bf16_bits_to_f64(inp["k"][cu[b]:cu[b + 1], g]),
-                             bf16_bits_to_f64(inp["v"][cu[b]:cu[b + 1], g]))
-        kg, vg = cache[(b, g)]
-        i = int(rng.integers(L))
-        qi = bf16_bits_to_f64(inp["q"][cu[b] + i, h])
-        t1 = time.perf_counter()
-        OA.row_attention(qi, kg, vg, i, mode, cfg.softmax_scale, sink=cfg.ssa_sink,
-                         window=cfg.ssa_window, block=cfg.block)
-        t_work += time.perf_counter() - t1
-        n_keys = (i + 1) if mode == 0 else (min(i + 1, cfg.ssa_sink) +
-                                            max(0, i - max(i - cfg.ssa_window + 1, cfg.ssa_sink) + 1))
-        flops += 4.0 * cfg.head_dim * n_keys
-        rows += 1
-    return dict(value=flops / t_work / 1e12, unit="TFLOP/s", cores=int(threads),
-                kind="oracle",
-                sample=f"{rows} random query rows of {cfg.name} (FA/SSA heads, fp64 numpy, "
-                       f"one row per call); pair-level flops / oracle time; "
-                       f"{len(os.sched_getaffinity(0))} host cores visible, "
-                       f"wall {time.perf_counter() - t0:.1f} s")
+        flops += 4.0 * cfg.head_dim * _head_pairs(cfg, L, int(inp["modes"][b, h // G]))
+        done.append((b, h))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    wall = time.perf_counter() - t0
+    kinds = {0: "FA", 1: "SSA"}
+    desc = ", ".join(f"seq {b} q-head {h} ({kinds[int(inp['modes'][b, h // G])]})" for b, h in done)
+    return dict(value=flops / wall / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"every query row of {len(done)} whole q-head(s) of {cfg.name}: {desc}; fp64 numpy "
+                       f"oracle (head_attention over row ranges, {threads} threads, single-threaded BLAS "
+                       f"per task); pair-level flops / wall {wall:.1f} s; "
+                       f"{len(os.sched_getaffinity(0))} host cores visible")
+
+
+def oracle_timing(names, threads):
+    """Wall time of the whole fp64 oracle layer (every row of every FA / SSA
+    q-head) per workload, with `threads` host threads."""
+    from synth import get_config, make_inputs
+    out = []
+    for name in names:
+        inp = make_inputs(get_config(name))
+        cfg = inp["cfg"]
+        G = cfg.gqa
+        heads = [(b, h) for b in range(len(inp["seqlens"])) for h in range(cfg.num_q_heads)
+                 if int(inp["modes"][b, h // G]) in (0, 1) and inp["seqlens"][b] > 0]
+        t0 = time.perf_counter()
+        _oracle_head_rows(inp, heads, threads)
+        wall = time.perf_counter() - t0
+        flops = sum(4.0 * cfg.head_dim * _head_pairs(cfg, int(inp["seqlens"][b]), int(inp["modes"][b, h // G]))
+                    for b, h in heads)
+        rec = {"workload": name, "threads": threads, "heads": len(heads), "wall_s": round(wall, 2),
+               "gflops": round(flops / wall / 1e9, 2)}
+        print(json.dumps(rec), flush=True)
+        out.append(rec)
+    return out
 
 
 def decode_bench(cfg, mode_row, L, batch, steps, warmup):
@@ -382,6 +439,11 @@ def main():
         return
     if a.traffic_from:
         write_traffic(a.traffic_from, a.config)
+        return
+    if a.oracle_timing:
+        names = a.oracle_timing.split(",")
+        oracle_timing(names, 1)
+        oracle_timing(names, max(1, min(16, len(os.sched_getaffinity(0)))))
         return
     if a.serial_sweep:
         if a.gpus != 1:

@@ -79,18 +79,25 @@ def _softmax_rows(s, allowed, vj):
 
 
 def head_attention(qh, kh, vh, mode, scale, sink=0, window=1, block=None,
-                   xa_mask=None, chunk=512):
-    """One (sequence, query head): qh [L,d], kh/vh [L,d] float64 -> o [L,d], lse [L]."""
+                   xa_mask=None, chunk=512, row_range=None):
+    """One (sequence, query head): qh [L,d], kh/vh [L,d] float64 -> o [L,d], lse [L].
+
+    row_range = (r0, r1) computes only query rows r0 <= i < r1 (returned as
+    o [r1 - r0, d], lse [r1 - r0]), so that the rows of one long head can be
+    split over host threads; each row is the same sum, up to the rounding
+    order of the matrix products over a differently cut chunk.
+    """
     L, d = qh.shape
-    o = np.empty((L, d), dtype=np.float64)
-    lse = np.empty(L, dtype=np.float64)
-    for i0 in range(0, L, chunk):
-        i1 = min(L, i0 + chunk)
+    r0, r1 = (0, L) if row_range is None else (int(row_range[0]), int(row_range[1]))
+    o = np.empty((r1 - r0, d), dtype=np.float64)
+    lse = np.empty(r1 - r0, dtype=np.float64)
+    for i0 in range(r0, r1, chunk):
+        i1 = min(r1, i0 + chunk)
         ii = np.arange(i0, i1)
         jj = _candidate_keys(mode, i0, i1, sink, window)
         allowed = allowed_matrix(mode, ii, jj, L, sink, window, block, xa_mask)
         s = scale * (qh[i0:i1] @ kh[jj].T)
-        o[i0:i1], lse[i0:i1] = _softmax_rows(s, allowed, vh[jj])
+        o[i0 - r0:i1 - r0], lse[i0 - r0:i1 - r0] = _softmax_rows(s, allowed, vh[jj])
     return o, lse
 
 

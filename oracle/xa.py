@@ -133,10 +133,16 @@ def tie_info(P_row, I, tau_num, tau_den, cum_eps=1e-4, gap_rel=1e-5):
     """Boundary-tie diagnostics of block row I under the fp64 masses.
 
     Sorted as the selector sorts, with the cut after position k:
-      cum_tie  |C_{k-1} - tau| < cum_eps or |C_k - tau| < cum_eps
-               (the pages' threshold boundary; counted and reported);
-      gap_tie  the last kept and first dropped masses differ by less than
-               gap_rel * P_(k) (the order at the cut is within rounding).
+      cum_tie    |C_{k-1} - tau| < cum_eps or |C_k - tau| < cum_eps
+                 (the pages' threshold boundary; counted and reported);
+      gap_tie    the last kept and first dropped masses differ by less than
+                 gap_rel * P_(k) (the order at the cut is within rounding);
+      round_tie  a kept block whose weight is at most 1 above the first
+                 dropped block's, or a dropped block whose weight is at most 1
+                 below the last kept block's, has P * 2^24 within
+                 gap_rel * P * 2^24 of a rounding boundary (n + 1/2): one
+                 rounding step of its weight can move it across the cut, so
+                 the order at the cut is within rounding too.
     """
     tau = tau_num / tau_den
     w = quantize(P_row[: I + 1])
@@ -149,7 +155,16 @@ def tie_info(P_row, I, tau_num, tau_den, cum_eps=1e-4, gap_rel=1e-5):
     c_prev = C[k - 1] if k > 0 else 0.0
     cum_tie = abs(c_prev - tau) < cum_eps or abs(C[k] - tau) < cum_eps
     gap_tie = (k + 1 < len(p)) and (p[k] - p[k + 1] < gap_rel * p[k])
-    return dict(k=k, cum_tie=bool(cum_tie), gap_tie=bool(gap_tie),
+    round_tie = False
+    if k + 1 < len(p):
+        x = np.asarray(P_row[: I + 1], dtype=np.float64) * float(1 << QUANT_BITS)
+        near_half = np.abs(x - np.floor(x) - 0.5) < gap_rel * np.maximum(x, 1.0)
+        wk, wn = int(w[order[k]]), int(w[order[k + 1]])
+        kept = np.zeros(I + 1, dtype=bool)
+        kept[order[: k + 1]] = True
+        can_cross = np.where(kept, w <= wn + 1, w >= wk - 1)
+        round_tie = bool((near_half & can_cross).any())
+    return dict(k=k, cum_tie=bool(cum_tie), gap_tie=bool(gap_tie), round_tie=round_tie,
                 c_prev=float(c_prev), c_k=float(C[k]))
 
 

@@ -151,3 +151,21 @@ def test_prefill_rows_match_full():
     for n, (b, h, i) in enumerate(rows):
         np.testing.assert_allclose(o[n], O[cu[b] + i, h], atol=1e-13)
         assert abs(l[n] - LSE[h, cu[b] + i]) < 1e-13
+
+
+@pytest.mark.parametrize("mode", [MODE_FA, MODE_SSA, MODE_XA])
+def test_row_range_is_the_same_rows(mode):
+    # Restricting the computed query rows changes nothing in them beyond the
+    # rounding order of the chunked products (the rows of one long head can
+    # then be split over threads).
+    L, d, B = 300, 8, 16
+    q, k, v = _rand(L, d, 9)
+    nb = -(-L // B)
+    bm = np.tril(np.random.default_rng(4).random((nb, nb)) < 0.6)
+    bm[np.arange(nb), np.arange(nb)] = True
+    kw = dict(sink=7, window=40, block=B, xa_mask=bm, chunk=64)
+    o, lse = OA.head_attention(q, k, v, mode, 0.3, **kw)
+    for r0, r1 in ((0, 300), (17, 131), (299, 300), (64, 128)):
+        o2, l2 = OA.head_attention(q, k, v, mode, 0.3, row_range=(r0, r1), **kw)
+        np.testing.assert_allclose(o2, o[r0:r1], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l2, lse[r0:r1], rtol=0, atol=1e-13)

@@ -291,3 +291,45 @@ def test_mutant_partial_block_diagonal_only(monkeypatch):
     monkeypatch.setattr(OX, "head_mask", diag_only)
     with pytest.raises(AssertionError):
         TX.test_partial_last_block_is_fa(77)
+
+
+def test_mutant_tie_without_weight_rounding(monkeypatch):
+    orig = OX.tie_info
+
+    def no_round(P_row, I, tn, td, cum_eps=1e-4, gap_rel=1e-5):
+        t = orig(P_row, I, tn, td, cum_eps=cum_eps, gap_rel=gap_rel)
+        t["round_tie"] = False                                                          # planted
+        return t
+    monkeypatch.setattr(OX, "tie_info", no_round)
+    with pytest.raises(AssertionError):
+        TX.test_tie_info_weight_rounding_at_the_cut()
+
+
+def test_mutant_tie_rounding_any_weight(monkeypatch):
+    orig = OX.tie_info
+
+    def any_weight(P_row, I, tn, td, cum_eps=1e-4, gap_rel=1e-5):
+        t = orig(P_row, I, tn, td, cum_eps=cum_eps, gap_rel=gap_rel)
+        x = np.asarray(P_row[: I + 1]) * float(1 << 24)
+        t["round_tie"] = t["round_tie"] or bool((np.abs(x - np.floor(x) - 0.5) < 1e-5 * x).any())  # planted
+        return t
+    monkeypatch.setattr(OX, "tie_info", any_weight)
+    with pytest.raises(AssertionError):
+        TX.test_tie_info_weight_rounding_at_the_cut()
+
+
+def test_mutant_tie_rounding_near_cut_weight(monkeypatch):
+    orig = OX.tie_info
+
+    def near_cut_weight(P_row, I, tn, td, cum_eps=1e-4, gap_rel=1e-5):
+        t = orig(P_row, I, tn, td, cum_eps=cum_eps, gap_rel=gap_rel)
+        w = OX.quantize(P_row[: I + 1])
+        order = np.lexsort((np.arange(I + 1), -w))
+        x = np.asarray(P_row[: I + 1]) * float(1 << 24)
+        near = np.abs(x - np.floor(x) - 0.5) < 1e-5 * x
+        wk = w[order[t["k"]]]
+        t["round_tie"] = t["round_tie"] or bool((near & (np.abs(w - wk) <= 1)).any())     # planted
+        return t
+    monkeypatch.setattr(OX, "tie_info", near_cut_weight)
+    with pytest.raises(AssertionError):
+        TX.test_tie_info_heavy_block_at_a_rounding_boundary_is_no_tie()

@@ -352,3 +352,49 @@ def test_partial_last_block_is_fa(L):
     np.testing.assert_array_equal(lx, lf)
     # Its pair count is the causal triangle of L tokens.
     assert OX.kept_pairs(M, L, B) == L * (L + 1) // 2
+
+
+def test_tie_info_weight_rounding_at_the_cut():
+    # A flat row whose last kept block scales to 4998.3 (weight 4998) and
+    # whose first dropped block scales to 4997.4996 (weight 4997, 0.0004 below
+    # the rounding boundary): fp32 masses can round that block up to 4998,
+    # where the J-ascending order puts it first.  The masses differ by
+    # 1.7e-4 relative, so the gap rule does not see it; the rounding rule does.
+    S = float(1 << 24)
+
+    def row(x_drop):
+        # Head masses sum to tau - 1.5e-4, so the prefix crosses tau on the
+        # 4998.3 block; 400 light blocks (weight ~4176) follow the cut.
+        head = [0.4, 0.3, 0.9 - 1.5e-4 - 0.7]
+        n_tail = 400
+        rest = (1.0 - sum(head) - 4998.3 / S - x_drop / S) / (n_tail + 1)
+        P = np.array([rest] + head + [4998.3 / S, x_drop / S] + [rest] * n_tail)
+        return P, len(P) - 1
+    P, I = row(4997.4996)
+    t = OX.tie_info(P, I, 9, 10)
+    order = np.lexsort((np.arange(I + 1), -OX.quantize(P)))
+    assert order[t["k"]] == 4 and order[t["k"] + 1] == 5          # the two blocks sit at the cut
+    assert t["round_tie"] and not t["gap_tie"] and not t["cum_tie"]
+    P, I = row(4997.3)                                             # far from the boundary
+    t = OX.tie_info(P, I, 9, 10)
+    assert not t["round_tie"] and not t["gap_tie"] and not t["cum_tie"]
+    # A block near a rounding boundary far from the cut weight is no tie.
+    P, I = row(4997.3)
+    P[7] = 1234.4999 / S
+    P[0] -= (P.sum() - 1.0)
+    t = OX.tie_info(P, I, 9, 10)
+    assert not t["round_tie"]
+
+
+def test_tie_info_heavy_block_at_a_rounding_boundary_is_no_tie():
+    # A peaked row: the last kept block scales to exactly n + 1/2, but the
+    # first dropped block is far below it, so no rounding step can cross the
+    # cut (the masses' relative precision matters only through the gap rule).
+    S = float(1 << 24)
+    heavy = 5_035_000.5 / S                    # 0.3001..., weight 5,035,001
+    P = np.array([0.01, 0.6, heavy] + [(1.0 - 0.61 - heavy) / 30] * 30)
+    I = len(P) - 1
+    t = OX.tie_info(P, I, 9, 10)
+    order = np.lexsort((np.arange(I + 1), -OX.quantize(P)))
+    assert order[t["k"]] == 2 and not t["cum_tie"] and not t["gap_tie"]   # 0.6 + 0.3001 passes tau
+    assert not t["round_tie"]

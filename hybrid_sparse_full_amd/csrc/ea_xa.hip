@@ -29,16 +29,29 @@ __device__ inline int64_t tri_root(int64_t loc) {
 // stage is staged once and serves all HPI heads.  With GROUP (one mask per
 // KV head, HPI == G) the 8 waves split one tile and each accumulates the
 // products of all HPI heads into the same registers: the sum of the heads'
-// scores, divided by HPI in the epilogue, is the group-mean score.  A stage is KC = 64 elements
-// of the S * d reduction (one key row t of the antidiagonal, 64 of d); rows
-// of a staged tile are 128 bytes, 16-byte chunks XOR-swizzled by row % 8.
+// scores, divided by HPI in the epilogue, is the group-mean score.
+//
+// A stage is KC = 64 elements of the S * d reduction (part of one key row t
+// of the antidiagonal); the stages of an item stream through an LDS ring of
+// NS slots by global->LDS DMA, NS - 1 stages ahead of the MFMAs (two 80 KB
+// stages with four heads per item; measured: halving KC to keep a four-stage
+// ring was 6 % slower, its extra barriers cost more than the deeper
+// prefetch hid).  Rows of a staged tile are KC * 2 bytes, RPL = 256 / (KC * 2) of
+// them share the 64 LDS banks; the 16-byte chunks of row r are XOR-swizzled
+// by (r / RPL) % CPR, which puts the 16 rows that one 16-lane group of a
+// 128-bit operand read touches on 16 distinct 4-bank groups (a swizzle by
+// r % CPR alone gives rows r and r + CPR the same banks).
 template <int D, int R, int HPI, bool GROUP = false>
 struct XaCfg {
   static constexpr int NW = 8;                   // waves per workgroup
   static constexpr int NT = NW * 64;
   static constexpr int KC = 64;                  // reduction elements per stage
   static constexpr int ROWB = KC * 2;            // bytes per staged row
-  static constexpr int OPB = XT * ROWB;          // one staged operand tile (16 KB)
+  static constexpr int CPR = KC / 8;             // 16-byte chunks per staged row
+  static constexpr int RPL = 256 / ROWB;         // staged rows per 64-bank line
+  static constexpr int RPG = 1024 / ROWB;        // staged rows per 1 KB DMA region
+  static constexpr int OPB = XT * ROWB;          // one staged operand tile
+  static constexpr int OPR = OPB / 1024;         // DMA regions per operand tile
   static constexpr int STAGE = (1 + HPI) * OPB;  // K~ then HPI Q~ tiles
   static constexpr int NS = HPI == 4 ? 2 : 3;    // stages in the LDS ring
   static constexpr int NI = STAGE / 1024 / NW;   // 1 KB DMA regions per wave per stage
@@ -50,7 +63,28 @@ struct XaCfg {
   static constexpr int NB = XT / BW / 32;        // 32-key MFMA tiles per wave
   static constexpr int KSTEPS = KC / 16;
   static_assert((STAGE / 1024) % NW == 0, "DMA regions must split evenly over waves");
+  static_assert(NS * STAGE <= 160 * 1024, "the ring must fit in LDS");
+  static_assert((NS - 2) * NI <= 63, "vmcnt holds at most 63");
 };
+
+// Wait until this wave's DMA of the current stage has landed, with `ahead`
+// later stages (at most NS - 2) allowed in flight, then join the barrier.
+template <int NI, int NS>
+__device__ inline void stage_wait(int ahead) {
+  if constexpr (NS >= 4) {
+    if (ahead >= 2) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(2 * NI) : "memory");
+      return;
+    }
+  }
+  if constexpr (NS >= 3) {
+    if (ahead >= 1) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(NI) : "memory");
+      return;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+}
 
 template <int D, int R, int HPI, bool GROUP>
 __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __restrict__ q,
@@ -75,12 +109,15 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
   const int nhg = d.Hq / HPI;
   const int nst = S * D / C::KC;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // DMA: lane l of a 1 KB region writes staged row l / 8, physical chunk
-  // l % 8, which holds logical chunk (l % 8) ^ (l / 8) (row % 8 = l / 8).
-  const int rr = lane >> 3, lch = (lane & 7) ^ rr;
-  // MFMA operand reads: lane reads row 32 t + l32 at logical chunk 2 s + half.
-  const uint32_t fa = (uint32_t)l32 * C::ROWB + ((uint32_t)(l32 & 7) >> 1 << 5) +
-                      (((uint32_t)half ^ (uint32_t)(l32 & 1)) << 4);
+  // DMA: lane l of a 1 KB region (RPG staged rows) writes row l / CPR of the
+  // region, physical chunk l % CPR, which holds logical chunk
+  // (l % CPR) ^ ((row / RPL) % CPR).
+  const int rr = lane / C::CPR;
+  // MFMA operand reads: lane reads row 32 t + l32 at logical chunk 2 s + half,
+  // physical chunk (2 s + half) ^ ((l32 / RPL) % CPR) (32 t / RPL is a
+  // multiple of CPR); the 2 s part is XORed in per k-step.
+  const uint32_t fa = (uint32_t)l32 * C::ROWB +
+                      (((uint32_t)half ^ ((uint32_t)(l32 / C::RPL) % C::CPR)) << 4);
   volatile int64_t* item_box = (volatile int64_t*)smem;
 
   while (true) {
@@ -110,7 +147,8 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
       const int jj = wv * C::NI + i;
-      const int op = jj / 16, row = 8 * (jj % 16) + rr;
+      const int op = jj / C::OPR, row = C::RPG * (jj % C::OPR) + rr;
+      const int lch = (lane % C::CPR) ^ ((row / C::RPL) % C::CPR);
       gop[i] = (uint32_t)op;
       if (op == 0) {
         const int64_t bp = min(b0 + row, nred - 1);
@@ -123,21 +161,23 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
       }
     }
     // Stage st: t = st * KC / D, dk = st * KC % D; K~ walks t backwards.
-    auto issue = [&](int st) {
+    // DMA instruction i of this wave for stage st.
+    auto issue_one = [&](int st, int i) __attribute__((always_inline)) {
       const int t = st * C::KC / D, dk = st * C::KC % D;
       const int64_t dK = ((int64_t)(-t) * d.Hkv * D + dk) * 2;
       const int64_t dQ = ((int64_t)t * d.Hq * D + dk) * 2;
       const uint32_t slot = lds0 + (uint32_t)(st % C::NS) * C::STAGE;
+      const int jj = wv * C::NI + i;
+      const uint64_t ga = gaddr[i] + (uint64_t)(gop[i] == 0 ? dK : dQ);
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(slot + (uint32_t)jj * 1024u);
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(ga), "s"(m0v)
+                   : "m0");
+    };
+    auto issue = [&](int st) {
 #pragma unroll
-      for (int i = 0; i < C::NI; ++i) {
-        const int jj = wv * C::NI + i;
-        const uint64_t ga = gaddr[i] + (uint64_t)(gop[i] == 0 ? dK : dQ);
-        const uint32_t m0v = __builtin_amdgcn_readfirstlane(slot + (uint32_t)jj * 1024u);
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(ga), "s"(m0v)
-                     : "m0");
-      }
+      for (int i = 0; i < C::NI; ++i) issue_one(st, i);
     };
 
     f32x16 acc[C::NA][C::NB];
@@ -155,11 +195,16 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
       // Stage st has landed (own DMA) once at most the later stages' are in
       // flight; the barrier extends that to every wave and frees the slot
       // the next issue overwrites.
-      if (C::NS == 3 && st + 1 < nst)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(C::NI) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
-      if (st + C::NS - 1 < nst) issue(st + C::NS - 1);
+      stage_wait<C::NI, C::NS>(min(C::NS - 2, nst - 1 - st));
+      // The DMA of stage st + NS - 1 goes out between this stage's first
+      // MFMAs, one instruction after every second (measured 2 % faster than
+      // issuing it in one burst before them, and than one per MFMA or per
+      // three).  The DMA is what limits this loop: without it a stage runs
+      // at the MFMA rate, with it at ~60 % (its L2 misses outlast a stage).
+      const bool dnext = st + C::NS - 1 < nst;
+      const int snext = st + C::NS - 1;
+      constexpr int MPS = C::KSTEPS * C::NHQ * C::NA * C::NB;  // MFMAs per stage
+      constexpr int EVERY = 2;
       const uint32_t slot = (uint32_t)(st % C::NS) * C::STAGE;
       const uint8_t* Ks = smem + slot + (size_t)wb * (C::NB * 32) * C::ROWB;
       const uint8_t* Qs = smem + slot + (size_t)(1 + hh) * C::OPB + (size_t)wa * (C::NA * 32) * C::ROWB;
@@ -189,9 +234,20 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
 #pragma unroll
           for (int i = 0; i < C::NA; ++i)
 #pragma unroll
-            for (int j = 0; j < C::NB; ++j)
+            for (int j = 0; j < C::NB; ++j) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[s & 1][j], fq[s & 1][u][i], acc[i][j], 0, 0, 0);
+              const int mi = ((s * C::NHQ + u) * C::NA + i) * C::NB + j;
+              if (mi % EVERY == EVERY - 1 && mi / EVERY < C::NI) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (dnext) issue_one(snext, mi / EVERY);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
       }
+      // Instructions the interleave did not place (NI > MPS).
+#pragma unroll
+      for (int i = MPS / EVERY; i < C::NI; ++i)
+        if (dnext) issue_one(snext, i);
     }
 
     // Epilogue: per (reduced row a, block J) log-sum-exp in log2 units.

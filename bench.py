@@ -79,15 +79,23 @@ def calibrate_copy():
 
 def _counter_means(folder, counter):
     """Mean counter value (KiB per dispatch) per kernel name, from the
-    *_counter_collection.csv files rocprofv3 wrote under `folder`."""
+    *_counter_collection.csv files rocprofv3 wrote under `folder`, over the
+    dispatches of each kernel with its largest grid (the whole layer: the
+    serial-dispatch leg launches the same kernel on smaller sub-layers)."""
     import csv
     import glob
     vals = {}
     for f in glob.glob(os.path.join(folder, "**", "*_counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter:
-                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    return {k: (float(np.mean(v)), len(v)) for k, v in vals.items()}
+                vals.setdefault(r["Kernel_Name"], []).append((int(r.get("Grid_Size") or 0),
+                                                             float(r["Counter_Value"])))
+    out = {}
+    for k, v in vals.items():
+        g = max(x[0] for x in v)
+        sel = [x[1] for x in v if x[0] == g]
+        out[k] = (float(np.mean(sel)), len(sel))
+    return out
 
 
 def write_traffic(base, cfg_name):

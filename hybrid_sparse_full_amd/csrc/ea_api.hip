@@ -190,7 +190,12 @@ int64_t ea_workspace_offset(const ea_attn_desc* desc, int op, const char* name) 
 }
 
 const char* ea_status_string(ea_status s) {
-  switch (s) {
+  // A C caller may pass any int: read the argument's bytes instead of loading
+  // it as the enum (out-of-range enum values are undefined behaviour in C++).
+  int v;
+  static_assert(sizeof(v) == sizeof(s), "ea_status is int-sized");
+  std::memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case EA_OK: return "EA_OK";
     case EA_ERR_INVALID_ARG: return "EA_ERR_INVALID_ARG: invalid argument";
     case EA_ERR_UNSUPPORTED: return "EA_ERR_UNSUPPORTED: configuration not built";

@@ -346,3 +346,45 @@ def test_xa_block_sum_masses(group):
 
 def test_xassa_64k_r1_sampled():
     _sampled_check("xassa-64k-r1", 192, 5)
+
+
+def test_every_output_row_written():
+    # O and LSE are filled with NaN before the call: afterwards every token of
+    # every q-head must hold a finite value (each query attends at least its
+    # own key), in every mode, on a ragged batch with empty and one-token
+    # sequences; the same for the serial dispatch and the decode step.
+    import torch
+    from hybrid_sparse_full_amd import ea as E
+    from hybrid_sparse_full_amd.layer import HybridPrefill, HybridDecode, bf16_tensor, desc_for
+    dev = torch.device("cuda:0")
+    modes = ((MODE_FA, MODE_SSA), (MODE_XA, MODE_SSA), (MODE_SSA, MODE_XA), (MODE_XA, MODE_FA), (MODE_XA, MODE_XA))
+    cfg = _small(name="written", seqlens=(3 * 128 + 5, 1, 0, 700, 5 * 128), modes=modes)
+    inp = make_inputs(cfg)
+    desc = desc_for(cfg, inp["seqlens"])
+    layer = HybridPrefill(desc, inp["cu_seqlens"], inp["modes"], device=dev)
+    q, k, v = (bf16_tensor(inp[n], dev) for n in ("q", "k", "v"))
+    layer.o.fill_(float("nan"))
+    layer.lse.fill_(float("nan"))
+    layer(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(layer.o.float()).all() and torch.isfinite(layer.lse).all()
+    # Serial dispatch (FA / SSA heads only).
+    cfg2 = _small(name="written-serial", seqlens=(3 * 128 + 5, 1, 0, 700), modes=((MODE_SSA, MODE_FA),))
+    inp2 = make_inputs(cfg2)
+    d2 = desc_for(cfg2, inp2["seqlens"])
+    q2, k2, v2 = (bf16_tensor(inp2[n], dev) for n in ("q", "k", "v"))
+    o2 = torch.full((d2.total_tokens, d2.num_q_heads, d2.head_dim), float("nan"), dtype=torch.bfloat16, device=dev)
+    l2 = torch.full((d2.num_q_heads, d2.total_tokens), float("nan"), dtype=torch.float32, device=dev)
+    ws2 = torch.empty(E.ea_workspace_bytes(d2, E.EA_OP_PREFILL_SERIAL), dtype=torch.uint8, device=dev)
+    cu2 = torch.from_numpy(inp2["cu_seqlens"].astype(np.int32)).to(dev)
+    E.ea_hybrid_attn_prefill_serial(d2, q2, k2, v2, cu2, np.ascontiguousarray(inp2["modes"][0]), o2, l2, ws2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all() and torch.isfinite(l2).all()
+    # Decode: empty sequences give o = 0 and lse = -inf; nothing stays NaN.
+    dec = HybridDecode(desc, inp["cu_seqlens"], inp["modes"], device=dev)
+    dec.o.fill_(float("nan"))
+    dec.lse.fill_(float("nan"))
+    qn = bf16_tensor(inp["q"][np.maximum(inp["cu_seqlens"][1:] - 1, 0)], dev)
+    dec(qn, k, v)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dec.o.float()).any() and not torch.isnan(dec.lse).any()

@@ -78,10 +78,12 @@ size_t ws_layout(const EaDims& d, int op, WsLayout* L) {
   L->qb2seq = take(4 * (size_t)d.nqb_max);
   L->scal = take(4 * (size_t)SCAL_COUNT);
   if (op == EA_OP_DECODE) {
-    if (decode_waves(d) > 0x7fffffff) return 0;  // rejected by the decode call
+    if (decode_groups(d) > 0x7fffffff) return 0;  // rejected by the decode call
+    const size_t parts = (size_t)d.nseq * d.Hq * (size_t)decode_parts(d);
     L->dec_plan = take(8);
-    L->dec_waves = take(8 * (size_t)decode_waves(d));
-    L->dec_part = take(4 * (size_t)d.nseq * d.Hq * (size_t)decode_splits(d) * (d.D + 2));
+    L->dec_groups = take(8 * (size_t)decode_groups(d));
+    L->dec_part = take(4 * parts * d.D);
+    L->dec_ml = take(8 * parts);
     L->total = off;
     return off;
   }
@@ -404,7 +406,7 @@ static ea_status decode_check(const ea_attn_desc* desc, const void* q_dev, const
       ((uintptr_t)lse_out_dev & 3u))
     return EA_ERR_INVALID_ARG;
   if (d->nseq > 65535 || d->Hkv > 65535) return EA_ERR_UNSUPPORTED;
-  if (decode_waves(*d) > 0x7fffffff) return EA_ERR_UNSUPPORTED;
+  if (decode_groups(*d) > 0x7fffffff) return EA_ERR_UNSUPPORTED;
   *need = ws_layout(*d, EA_OP_DECODE, L);
   return EA_OK;
 }

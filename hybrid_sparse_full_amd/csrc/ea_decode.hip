@@ -8,18 +8,20 @@
 // A decode step reads each kept K/V row once and does 4 d flops per key and
 // q-head, ~4 flop per byte: it is bound by HBM bandwidth, so it runs on the
 // vector ALU with bf16 dot products, not on the matrix core.  Design:
-//   * split-K over waves: one wave takes a split of 256 to 4096 kept-key
+//   * split-K over waves: one wave takes a split of 64 to 4096 kept-key
 //     positions of one (sequence, KV head) for
 //     GW of its q-heads (all G when G <= 8), so each
 //     K/V row is read once per GW heads.  The key set is compressed: an SSA
 //     head's first split covers the sink and the start of the window.
 //     The split length comes from the kept keys of the whole step: when the
 //     modes could change it, a one-workgroup plan kernel sums them, picks
-//     the split and lists the waves that have work, so a step whose heads
-//     are mostly SSA still spreads over as many waves as an all-FA one, and
-//     no idle wave sits between busy ones in the grid (the rest of the grid,
-//     sized for the shortest split, ends at once).  Waves are independent:
-//     no LDS staging and no workgroup barrier;
+//     the split and lists the workgroups that have work, so a step whose
+//     heads are mostly SSA still spreads over as many waves as an all-FA
+//     one, and no idle workgroup sits between busy ones in the grid (the
+//     rest of the grid, sized for the shortest split, ends at once).  The
+//     DEC_WPG waves of a workgroup take consecutive splits of one
+//     (sequence, KV head, head group); they stream their keys independently
+//     and meet once, at the end, to merge their results in LDS;
 //   * lane layout: a key row of d bf16 is spread over d / 8 lanes, 16 bytes
 //     each, so one wave load moves 64 / (d / 8) whole rows (contiguous 2 d
 //     bytes per row) of K and of V;
@@ -30,9 +32,10 @@
 //     block in the exp2 domain; P is rounded to bf16 and P V uses one
 //     v_dot2_f32_bf16 per pair of iterations and column (the pairs built
 //     with v_perm_b32), while the row sum stays in fp32;
-//   * each wave writes (m, l, unnormalised o) of its split in fp32; a second
-//     kernel combines the splits of every (sequence, q-head) into o (bf16)
-//     and lse (fp32).
+//   * each workgroup writes one partial (m, l, unnormalised o) in fp32 for
+//     each of its heads; a second kernel combines the partials of every
+//     (sequence, q-head) into o (bf16) and lse (fp32) in one online pass,
+//     with the 16-byte loads of many partials in flight per thread.
 #include "ea_device.h"
 
 namespace ea {
@@ -46,16 +49,21 @@ struct DecArgs {
   const uint16_t* v;
   const int32_t* cu;
   const uint8_t* modes;
-  float* part;         // [nseq, Hq, nsplit_max, D + 2]
-  const int32_t* plan;  // null: split is fixed; else [0] split, [1] listed waves
-  const int2* wlist;    // (unit, split) per listed wave, unit = (b Hkv + g) (G / GW) + wg
+  float* part;         // unnormalised o of each partial: [nseq, Hq, nparts, D]
+  float2* ml;          // (m, l) of each partial: [nseq, Hq, nparts]
+  const int32_t* plan;  // null: split is fixed; else [0] split, [1] listed workgroups
+  const int2* glist;    // (unit, partial) per listed workgroup, unit = (b Hkv + g) (G / GW) + wg
+  // Plan inside k_decode (few units): split = rule over the kept keys, no
+  // lower than `split`; workgroup 0 stores it in plan_out[0] for the combine.
+  int32_t* plan_out;
+  int32_t inline_plan;
   // Segmented cache (null: k / v are the packed [T, Hkv, D] cache): rows of
   // (sequence b, KV head g) are [seg[b Hkv + g], seg[b Hkv + g + 1]) of a
   // head-major [cache_rows, D] pool; an SSA segment is a ring of its sink and
   // window keys (key j >= sink in slot sink + (j - sink) mod window).
   const int64_t* seg;
   int64_t cache_rows;
-  int32_t nseq, Hq, Hkv, G, T, maxL, sink, window, split, nsplit_max;
+  int32_t nseq, Hq, Hkv, G, T, maxL, sink, window, split, nparts;
   float c2;            // softmax scale * log2(e)
 };
 
@@ -141,15 +149,19 @@ __device__ inline int32_t dec_kept_at(const DecArgs& a, int64_t i) {
 
 // Plan of one decode step, one workgroup: the split (decode_split_rule over
 // the kept keys of every (sequence, KV head) times the nwg head groups, no
-// lower than s_min), then one wlist entry per wave that has work, units in
-// order, so those waves are a prefix of the grid.  plan[0] = split,
-// plan[1] = listed waves.  The list holds at most (units) * ceil(maxL /
-// s_min) entries, the grid's size.
+// lower than s_min), then one glist entry per workgroup that has work (a
+// workgroup covers DEC_WPG splits), units in order, so those workgroups are
+// a prefix of the grid.  plan[0] = split, plan[1] = listed workgroups.  The
+// list holds at most (units) * cdiv(maxL, DEC_WPG * s_min) entries, the
+// grid's size.  Units are taken 1024 at a time: a block scan of their
+// workgroup counts gives each unit its first entry, then every thread fills
+// entries and finds an entry's unit by binary search over those firsts.
 __global__ __launch_bounds__(1024) void k_decode_plan(DecArgs a, int32_t s_min, int32_t nwg,
-                                                      int32_t* plan, int2* wlist) {
+                                                      int32_t* plan, int2* glist) {
   __shared__ long long red[16];
   __shared__ int32_t wsum[16];
   __shared__ int32_t s_split;
+  __shared__ int32_t first[1024];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t nbg = (int64_t)a.nseq * a.Hkv;
   long long w = 0;
@@ -164,12 +176,12 @@ __global__ __launch_bounds__(1024) void k_decode_plan(DecArgs a, int32_t s_min, 
   }
   __syncthreads();
   const int32_t S = s_split;
-  // Exclusive scan of the per-unit split counts, 1024 units at a time.
+  const int64_t per = (int64_t)DEC_WPG * S;  // kept keys per workgroup
   const int64_t nu = nbg * nwg;
   int32_t base = 0;
   for (int64_t c0 = 0; c0 < nu; c0 += 1024) {
     const int64_t u = c0 + tid;
-    const int32_t cnt = u < nu ? cdiv(dec_kept_at(a, u / nwg), S) : 0;
+    const int32_t cnt = u < nu ? (int32_t)((dec_kept_at(a, u / nwg) + per - 1) / per) : 0;
     int32_t x = cnt;
     for (int off = 1; off < 64; off <<= 1) {
       const int32_t y = __shfl_up(x, off);
@@ -183,10 +195,17 @@ __global__ __launch_bounds__(1024) void k_decode_plan(DecArgs a, int32_t s_min, 
       before += i < wv ? v : 0;
       total += v;
     }
-    const int32_t first = base + before + x - cnt;
-    for (int32_t j = 0; j < cnt; ++j) wlist[first + j] = make_int2((int)u, j);
+    first[tid] = base + before + x - cnt;
+    __syncthreads();
+    // Entry e of this chunk belongs to its last unit whose first entry is at
+    // most e (a unit with no workgroups shares its first with the next one).
+    const int nloc = (int)(nu - c0 < 1024 ? nu - c0 : 1024);
+    for (int32_t e = base + tid; e < base + total; e += 1024) {
+      const int i = upper_index(first, nloc, e);
+      glist[e] = make_int2((int)(c0 + i), e - first[i]);
+    }
     base += total;
-    __syncthreads();  // wsum is rewritten by the next chunk
+    __syncthreads();  // first and wsum are rewritten by the next chunk
   }
   if (tid == 0) {
     plan[0] = S;
@@ -195,41 +214,75 @@ __global__ __launch_bounds__(1024) void k_decode_plan(DecArgs a, int32_t s_min, 
 }
 
 template <int D, int GW, bool SEG>
-__global__ __launch_bounds__(256) void k_decode(DecArgs a) {
+__global__ __launch_bounds__(DEC_WPG * 64) void k_decode(DecArgs a) {
   constexpr int LPK = D / 8;          // lanes per key row
   constexpr int KPI = 64 / LPK;       // keys per wave iteration
-  const int lane = threadIdx.x & 63;
+  constexpr int CPL = D / 64;         // merged columns per lane
+  // Each wave's (o, m, l) per head, merged once all waves are done.
+  __shared__ float red[DEC_WPG][GW][D + 2];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int grp = lane / LPK, pc = lane % LPK;
-  // Wave -> (split, head group, KV head, sequence): from the plan's list,
-  // else split fastest.
+  // Workgroup -> (partial, head group, KV head, sequence): from the plan's
+  // list, else partial fastest.  Every early return below is uniform over
+  // the workgroup, so all its waves reach the merge barrier.
   const int nwg = a.G / GW;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int32_t S, split;
+  int32_t S, part, s0, L;
   int64_t u;
-  if (a.plan) {
-    S = a.plan[0];
-    if (w >= a.plan[1]) return;  // wave-uniform
-    const int2 e = a.wlist[w];
-    u = e.x;
-    split = e.y;
+  int mode;
+  if (a.inline_plan) {
+    // Lane i holds unit i (at most 64 units): its sequence bounds, mode and
+    // workgroup count; the workgroup's unit is the number of units whose
+    // inclusive count is at most blockIdx.x.
+    const int nu = a.nseq * a.Hkv * nwg;
+    int64_t kept = 0;
+    int32_t us0 = 0, uL = 0, um = EA_MODE_FA;
+    if (lane < nu) {
+      const int bg = lane / nwg;
+      seq_bounds(a, bg / a.Hkv, &us0, &uL);
+      um = sane_mode(a.modes[bg]);
+      if (um == EA_MODE_XA) um = EA_MODE_FA;
+      kept = dec_kept(um, uL, a.sink, a.window);
+    }
+    S = decode_split_rule(wave_sum(kept), a.split);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.plan_out[0] = S;
+    const int64_t per = (int64_t)DEC_WPG * S;
+    const int32_t cnt = (int32_t)((kept + per - 1) / per);
+    const int32_t incl = wave_inclusive_sum(cnt);
+    if ((int)blockIdx.x >= __shfl(incl, 63)) return;
+    const int ui = __popcll(__ballot(incl <= (int)blockIdx.x));
+    part = (int)blockIdx.x - (__shfl(incl, ui) - __shfl(cnt, ui));
+    u = ui;
+    s0 = __shfl(us0, ui);
+    L = __shfl(uL, ui);
+    mode = __shfl(um, ui);
   } else {
-    S = a.split;
-    split = (int)(w % a.nsplit_max);
-    u = w / a.nsplit_max;
+    if (a.plan) {
+      S = a.plan[0];
+      if ((int64_t)blockIdx.x >= a.plan[1]) return;
+      const int2 e = a.glist[blockIdx.x];
+      u = e.x;
+      part = e.y;
+    } else {
+      S = a.split;
+      part = (int)(blockIdx.x % a.nparts);
+      u = blockIdx.x / a.nparts;
+    }
+    const int b = (int)(u / nwg / a.Hkv);
+    if (b >= a.nseq) return;
+    seq_bounds(a, b, &s0, &L);
+    mode = sane_mode(a.modes[(size_t)(u / nwg)]);
+    if (mode == EA_MODE_XA) mode = EA_MODE_FA;
   }
   const int wg = (int)(u % nwg);
   u /= nwg;
   const int g = (int)(u % a.Hkv);
   const int b = (int)(u / a.Hkv);
-  if (b >= a.nseq) return;
-  int32_t s0, L;
-  seq_bounds(a, b, &s0, &L);
-  int mode = sane_mode(a.modes[(size_t)b * a.Hkv + g]);
-  if (mode == EA_MODE_XA) mode = EA_MODE_FA;
   const int32_t n = dec_kept(mode, L, a.sink, a.window);
-  const int32_t p0 = split * S;
-  if (p0 >= n) return;  // wave-uniform
-  const int32_t p1 = p0 + min(S, n - p0);
+  const int64_t gbase = (int64_t)part * DEC_WPG * S;
+  if (gbase >= n) return;  // no partial of this workgroup is combined
+  // This wave's split; the last waves of a unit's last workgroup may get none.
+  const int32_t p0 = (int32_t)min<int64_t>(gbase + (int64_t)wv * S, n);
+  const int32_t p1 = (int32_t)min<int64_t>((int64_t)p0 + S, n);
   const int nit = (p1 - p0 + KPI - 1) / KPI;
   const int nblk = (nit + DEC_BI - 1) / DEC_BI;
   const int h0 = g * a.G + wg * GW;
@@ -345,7 +398,7 @@ __global__ __launch_bounds__(256) void k_decode(DecArgs a) {
 
   // Block blk lives in ring slot blk % 3; the body is unrolled three times so
   // that slots are compile-time register sets.
-  load_block(0, std::integral_constant<int, 0>());
+  if (nblk > 0) load_block(0, std::integral_constant<int, 0>());
   if (nblk > 1) load_block(1, std::integral_constant<int, 1>());
   auto body = [&](int blk, auto slot_c, auto next_c) {
     if (blk + 2 < nblk) load_block(blk + 2, next_c);
@@ -357,72 +410,122 @@ __global__ __launch_bounds__(256) void k_decode(DecArgs a) {
     if (blk + 2 < nblk) body(blk + 2, std::integral_constant<int, 2>(), std::integral_constant<int, 1>());
   }
 
-  // Sum the key groups (m is already wave-uniform) and write the split.
+  // Sum the key groups (m is already wave-uniform) and stage the split's
+  // result; a wave without keys stages m = -inf, l = 0, o = 0.
 #pragma unroll
   for (int hh = 0; hh < GW; ++hh) {
     const float lt = groups_sum<LPK>(l[hh]);
-    float* dst = a.part + (((size_t)b * a.Hq + h0 + hh) * a.nsplit_max + split) * (D + 2);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float oc = groups_sum<LPK>(o[hh][c]);
-      if (grp == 0) dst[8 * pc + c] = oc;
+      if (grp == 0) red[wv][hh][8 * pc + c] = oc;
     }
     if (lane == 0) {
-      dst[D] = m[hh];
-      dst[D + 1] = lt;
+      red[wv][hh][D] = m[hh];
+      red[wv][hh][D + 1] = lt;
     }
+  }
+  __syncthreads();
+  // Merge the workgroup's splits (wave w takes heads w, w + DEC_WPG, ...)
+  // into one partial; wave 0's split has keys, so M is finite.
+  for (int hh = wv; hh < GW; hh += DEC_WPG) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < DEC_WPG; ++i) M = fmaxf(M, red[i][hh][D]);
+    float Ls = 0.f, acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DEC_WPG; ++i) {
+      const float mi = red[i][hh][D];
+      const float wt = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+      Ls += wt * red[i][hh][D + 1];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += wt * red[i][hh][CPL * lane + c];
+    }
+    const size_t idx = ((size_t)b * a.Hq + h0 + hh) * a.nparts + part;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) a.part[idx * D + CPL * lane + c] = acc[c];
+    if (lane == 0) a.ml[idx] = make_float2(M, Ls);
   }
 }
 
-// Combine the splits of one (sequence, q-head).  256 threads: the split
-// maxima are reduced over the workgroup; then wave w folds splits w, w + 4,
-// ... (lanes own CPL columns, loads of several splits in flight) and the
-// four waves meet in LDS.
+// Combine the partials of one (sequence, q-head) in one online pass.  512
+// threads: a partial's o row is read by D / 4 threads (16 bytes each), so
+// 512 / (D / 4) partials are read side by side, and each thread issues the
+// loads of U of its partials before it uses any; each thread keeps a
+// running (m, l, o) over its partials, rescaled once per batch, and the
+// thread groups meet in LDS at the end.
 template <int D>
-__global__ __launch_bounds__(256) void k_decode_combine(DecArgs a, uint16_t* out, float* lse) {
-  constexpr int CPL = D / 64;
-  __shared__ float red[4 * (D + 2)];
-  __shared__ float mred[4];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+__global__ __launch_bounds__(512) void k_decode_combine(DecArgs a, uint16_t* out, float* lse) {
+  constexpr int TPR = D / 4;     // threads per partial row
+  constexpr int NGR = 512 / TPR; // partials side by side
+  constexpr int U = 16;          // partials per thread per batch
+  __shared__ float red[NGR][D + 2];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int gi = tid / TPR, j = tid % TPR;
   int32_t s0, L;
   seq_bounds(a, b, &s0, &L);
   int mode = sane_mode(a.modes[(size_t)b * a.Hkv + h / a.G]);
   if (mode == EA_MODE_XA) mode = EA_MODE_FA;
   const int32_t n = dec_kept(mode, L, a.sink, a.window);
-  const int32_t S = dec_split(a);
-  const int ns = cdiv(n, S);
-  const float* src = a.part + ((size_t)b * a.Hq + h) * a.nsplit_max * (D + 2);
-  float M = -INFINITY;
-  for (int s = tid; s < ns; s += 256) M = fmaxf(M, src[(size_t)s * (D + 2) + D]);
-  M = wave_max(M);
-  if (lane == 0) mred[wv] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
-  float Ls = 0.f, acc[CPL];
+  const int64_t per = (int64_t)DEC_WPG * dec_split(a);
+  const int ns = (int)((n + per - 1) / per);
+  const size_t row0 = ((size_t)b * a.Hq + h) * a.nparts;
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sb = gi; sb < ns; sb += NGR * U) {
+    float2 ml[U];
+    f32x4 ov[U];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-#pragma unroll 4
-  for (int s = wv; s < ns; s += 4) {
-    const float* row = src + (size_t)s * (D + 2);
-    const float w = __builtin_amdgcn_exp2f(row[D] - M);
-    Ls += w * row[D + 1];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] += w * row[CPL * lane + c];
-  }
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) red[wv * (D + 2) + CPL * lane + c] = acc[c];
-  if (lane == 0) red[wv * (D + 2) + D] = Ls;
-  __syncthreads();
-  if (wv == 0) {
-    const float Lt = red[D] + red[(D + 2) + D] + red[2 * (D + 2) + D] + red[3 * (D + 2) + D];
-    uint16_t* orow = out + ((size_t)b * a.Hq + h) * D;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int col = CPL * lane + c;
-      const float v = red[col] + red[(D + 2) + col] + red[2 * (D + 2) + col] + red[3 * (D + 2) + col];
-      orow[col] = __builtin_bit_cast(uint16_t, (__bf16)(ns > 0 ? v / Lt : 0.f));
+    for (int k = 0; k < U; ++k) {
+      const int s = sb + k * NGR;
+      if (s < ns) {
+        ml[k] = a.ml[row0 + s];
+        ov[k] = *(const f32x4*)(a.part + (row0 + s) * D + 4 * j);
+      } else {
+        ml[k] = make_float2(-INFINITY, 0.f);
+        ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    if (lane == 0) lse[(size_t)b * a.Hq + h] = ns > 0 ? (M + __log2f(Lt)) * LN2 : -INFINITY;
+    // Partial sb is inside [0, ns), so the batch maximum is finite.
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < U; ++k) mb = fmaxf(mb, ml[k].x);
+    const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mb);
+    l *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const float w = ml[k].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - mb);
+      l += w * ml[k].y;
+      acc += w * ov[k];
+    }
+    m = mb;
+  }
+  *(f32x4*)&red[gi][4 * j] = acc;
+  if (j == 0) {
+    red[gi][D] = m;
+    red[gi][D + 1] = l;
+  }
+  __syncthreads();
+  if (tid < TPR) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NGR; ++g) M = fmaxf(M, red[g][D]);
+    float Lt = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < NGR; ++g) {
+      const float mg = red[g][D];
+      const float w = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - M);
+      Lt += w * red[g][D + 1];
+      o += w * *(const f32x4*)&red[g][4 * tid];
+    }
+    const float inv = ns > 0 ? 1.0f / Lt : 0.f;
+    const bf16x4 hv = __builtin_convertvector(o * inv, bf16x4);
+    *(bf16x4*)(out + ((size_t)b * a.Hq + h) * D + 4 * tid) = hv;
+    if (tid == 0) lse[(size_t)b * a.Hq + h] = ns > 0 ? (M + __log2f(Lt)) * LN2 : -INFINITY;
   }
 }
 
@@ -536,6 +639,7 @@ hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, 
   a.cu = cu;
   a.modes = modes;
   a.part = (float*)((char*)ws + L.dec_part);
+  a.ml = (float2*)((char*)ws + L.dec_ml);
   a.nseq = d.nseq;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
@@ -544,24 +648,30 @@ hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, 
   a.maxL = d.maxL;
   a.sink = d.sink;
   a.window = d.window;
-  // Splits of at least decode_split_min: the partials hold nsplit_max of them
-  // per (sequence, q-head) and the grid one wave each.
+  // Splits of at least decode_split_min: the partials hold nparts of them
+  // per (sequence, q-head) and the grid one workgroup each.
   const int gw = decode_gw(d);
   a.split = decode_split_min(d);
-  a.nsplit_max = decode_splits(d);
+  a.nparts = decode_parts(d);
   a.plan = nullptr;
-  a.wlist = nullptr;
+  a.glist = nullptr;
+  a.plan_out = nullptr;
+  a.inline_plan = 0;
   a.c2 = d.scale * LOG2E;
-  if (a.nsplit_max > 0 && decode_split_max(d) > a.split) {
+  if (a.nparts > 0 && decode_split_max(d) > a.split) {
     int32_t* plan = (int32_t*)((char*)ws + L.dec_plan);
-    int2* wlist = (int2*)((char*)ws + L.dec_waves);
-    hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, st, a, a.split, d.G / gw, plan, wlist);
+    if ((int64_t)d.nseq * d.Hkv * (d.G / gw) <= DEC_INLINE_UNITS) {
+      a.inline_plan = 1;
+      a.plan_out = plan;
+    } else {
+      int2* glist = (int2*)((char*)ws + L.dec_groups);
+      hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, st, a, a.split, d.G / gw, plan, glist);
+      a.glist = glist;
+    }
     a.plan = plan;
-    a.wlist = wlist;
   }
-  if (a.nsplit_max > 0) {
-    const int64_t waves = decode_waves(d);
-    const dim3 grid((unsigned)((waves + 3) / 4));
+  if (a.nparts > 0) {
+    const dim3 grid((unsigned)decode_groups(d));
     void (*kern)(DecArgs) = nullptr;
     if (seg) {
       if (d.D == 128)
@@ -578,11 +688,11 @@ hipError_t launch_decode(const EaDims& d, const uint16_t* q, const uint16_t* k, 
         kern = gw == 8 ? k_decode<64, 8, false> : gw == 4 ? k_decode<64, 4, false>
              : gw == 2 ? k_decode<64, 2, false> : k_decode<64, 1, false>;
     }
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kern, grid, dim3(DEC_WPG * 64), 0, st, a);
   }
   const dim3 cgrid((unsigned)d.Hq, (unsigned)d.nseq);
-  if (d.D == 128) hipLaunchKernelGGL(k_decode_combine<128>, cgrid, dim3(256), 0, st, a, o, lse);
-  else hipLaunchKernelGGL(k_decode_combine<64>, cgrid, dim3(256), 0, st, a, o, lse);
+  if (d.D == 128) hipLaunchKernelGGL(k_decode_combine<128>, cgrid, dim3(512), 0, st, a, o, lse);
+  else hipLaunchKernelGGL(k_decode_combine<64>, cgrid, dim3(512), 0, st, a, o, lse);
   return hipGetLastError();
 }
 

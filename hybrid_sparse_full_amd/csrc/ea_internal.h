@@ -64,7 +64,7 @@ struct WsLayout {
   // prefill
   size_t kvp, unit_cost, row_cost, row_off, hist, cursor, sorted_units, tiles;
   // decode
-  size_t dec_plan, dec_waves, dec_part;
+  size_t dec_plan, dec_groups, dec_part, dec_ml;
   // serial dispatch: the inner prefill's workspace, then the split copies
   size_t ser_inner, ser_inner_bytes, ser_q, ser_k, ser_v, ser_o, ser_lse, ser_modes;
   size_t total;
@@ -88,18 +88,27 @@ hipError_t launch_worklist(const EaDims& d, const uint16_t* k, const uint16_t* v
 hipError_t launch_attention(const EaDims& d, const uint16_t* q, const uint8_t* modes, const SeqMeta& m, void* ws,
                             const WsLayout& L, uint16_t* o, float* lse, hipStream_t st);
 // Decode: kept-key positions per split (one wave each), a power of two in
-// [256, 4096].  The rule: the smallest split s with s * DEC_WAVES >= the
-// step's work, where work = sum over (sequence, KV head) of its kept keys
-// times the q-head groups per KV head (G / gw), so the step spreads over
-// about DEC_WAVES waves (8 per CU).  Longer splits amortise a wave's
+// [DEC_SPLIT_FLOOR, 4096].  The rule: the smallest split s with
+// s * DEC_WAVES >= the step's work, where work = sum over (sequence, KV head)
+// of its kept keys times the q-head groups per KV head (G / gw), so the step
+// spreads over about DEC_WAVES waves.  Longer splits amortise a wave's
 // pipeline start; more splits fill the chip when the batch is small.
 // The kept keys depend on the modes, which live in device memory: the host
 // bounds the work by the all-FA case (T keys per KV head), which gives the
 // largest split.  When that bound leaves a choice, k_decode_plan applies the
 // rule to the true work on the device (no lower than an eighth of the bound)
-// and lists the waves that have work, so no idle wave sits between them.
-// The grid, the wave list and the partials are sized for the smallest split.
+// and lists the workgroups that have work, so no idle one sits between them.
+// A workgroup of DEC_WPG waves takes DEC_WPG consecutive splits of one
+// (sequence, KV head, head group) and merges them in LDS into one partial,
+// so a (sequence, q-head) has cdiv(kept, DEC_WPG * split) partials to combine.
+// The grid, the list and the partials are sized for the smallest split.
+// With at most DEC_INLINE_UNITS (sequence, KV head, head group) units the
+// plan needs no kernel of its own: every wave applies the rule over one
+// lane per unit and finds its workgroup's unit by a scan and a ballot.
+constexpr int DEC_INLINE_UNITS = 64;
 constexpr int32_t DEC_WAVES = 2048;
+constexpr int32_t DEC_SPLIT_FLOOR = 64;
+constexpr int DEC_WPG = 4;
 inline int32_t decode_gw(const EaDims& d) {
   return d.G % 8 == 0 ? 8 : d.G % 4 == 0 ? 4 : d.G % 2 == 0 ? 2 : 1;
 }
@@ -108,18 +117,22 @@ __host__ __device__ inline int32_t decode_split_rule(int64_t work, int32_t s) {
   return s;
 }
 inline int32_t decode_split_max(const EaDims& d) {
-  return decode_split_rule((int64_t)d.T * d.Hkv * (d.G / decode_gw(d)), 256);
+  return decode_split_rule((int64_t)d.T * d.Hkv * (d.G / decode_gw(d)), DEC_SPLIT_FLOOR);
 }
 inline int32_t decode_split_min(const EaDims& d) {
   const int32_t s = decode_split_max(d) / 8;
-  return s < 256 ? 256 : s;
+  return s < DEC_SPLIT_FLOOR ? DEC_SPLIT_FLOOR : s;
 }
-inline int32_t decode_splits(const EaDims& d) { return cdiv(d.maxL, decode_split_min(d)); }
-// Waves of the decode grid: one per (split, head group, KV head, sequence),
-// saturated at 2^62 (the decode call rejects more than 2^31 - 1).
-inline int64_t decode_waves(const EaDims& d) {
-  const double w = (double)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_splits(d);
-  return w >= 4.6e18 ? ((int64_t)1 << 62) : (int64_t)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_splits(d);
+// Partials per (sequence, q-head): one per workgroup of DEC_WPG splits.
+inline int32_t decode_parts(const EaDims& d) {
+  return (int32_t)(((int64_t)d.maxL + (int64_t)DEC_WPG * decode_split_min(d) - 1) /
+                   ((int64_t)DEC_WPG * decode_split_min(d)));
+}
+// Workgroups of the decode grid: one per (partial, head group, KV head,
+// sequence), saturated at 2^62 (the decode call rejects more than 2^31 - 1).
+inline int64_t decode_groups(const EaDims& d) {
+  const double w = (double)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_parts(d);
+  return w >= 4.6e18 ? ((int64_t)1 << 62) : (int64_t)d.nseq * d.Hkv * (d.G / decode_gw(d)) * decode_parts(d);
 }
 // seg == nullptr: k / v are the packed [T, Hkv, D] cache; else the
 // segmented head-major cache of cache_rows rows (see ea_decode_cache_layout).

@@ -264,13 +264,14 @@ ea_status ea_sparsity_ratios(const ea_attn_desc* desc, const int32_t* cu_seqlens
  *         (sanitised on the device as for the prefill).
  * Outputs o_out_dev [num_seqs, Hq, d] bf16, lse_out_dev [num_seqs, Hq] fp32.
  * The descriptor's block / xa fields must be valid but are unused; Hq / Hkv
- * <= 16, num_seqs and Hkv <= 65535, and at most 2^31 - 1 key-split waves
- * (num_seqs * Hkv * ceil(max_seqlen / split) for the shortest split the
- * descriptor allows) (EA_ERR_UNSUPPORTED otherwise).
+ * <= 16, num_seqs and Hkv <= 65535, and at most 2^31 - 1 decode
+ * workgroups (num_seqs * Hkv * q-head groups * ceil(max_seqlen / (4 *
+ * split)) for the shortest key split the descriptor allows; a workgroup
+ * takes four splits) (EA_ERR_UNSUPPORTED otherwise).
  * Workspace: ea_workspace_bytes(desc, EA_OP_DECODE) bytes of device memory
- * (the step's split plan and wave list, fp32 partial results of the key
- * splits).  The step runs in stream order; concurrent calls need separate
- * workspaces.
+ * (the step's split plan and workgroup list, and one fp32 partial result
+ * per workgroup and q-head).  The step runs in stream order; concurrent
+ * calls need separate workspaces.
  */
 ea_status ea_hybrid_attn_decode(const ea_attn_desc* desc, const void* q_dev, const void* k_dev,
                                 const void* v_dev, const int32_t* cu_seqlens_dev,
@@ -356,15 +357,15 @@ ea_status ea_hybrid_attn_decode_cached(const ea_attn_desc* desc, const void* q_d
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, outputs, checks and results
  * are those of ea_hybrid_attn_decode (the same kernels run); the step's
- * scratch (split plan, wave list, fp32 split partials) lives instead in a
+ * scratch (split plan, workgroup list, fp32 partials) lives instead in a
  * device array of EA_DECODE_NOALLOC_SCRATCH_BYTES that the library owns, one
  * per GPU, held from the first call on that GPU until the process ends.
  * The call allocates nothing: no hipMalloc / hipFree and no allocating
  * library routine.
  * Limit: a step whose ea_workspace_bytes(desc, EA_OP_DECODE) exceeds
  * EA_DECODE_NOALLOC_SCRATCH_BYTES returns EA_ERR_WORKSPACE before any launch
- * (64 MiB holds, e.g., 8 or 16 sequences of 64K cached tokens, or 64 of 8K,
- * at 32/8 heads and d = 128).  The first call on a GPU looks up that GPU's
+ * (64 MiB holds, e.g., 64 sequences of 64K cached tokens, 512 of 8K, or
+ * one of 1M, at 32/8 heads and d = 128).  The first call on a GPU looks up that GPU's
  * array (EA_ERR_HIP if that fails).
  * Concurrency: every call on one GPU uses the same array, so calls whose
  * device work overlaps on one GPU (different streams, or host threads

@@ -141,7 +141,7 @@ int main() {
     const size_t wd = ea_workspace_bytes(&p, EA_OP_DECODE);
     EXPECT(ea_hybrid_attn_decode(&p, FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const uint8_t*)FAKE, FAKE,
                                  (float*)FAKE, FAKE, wd - 1, nullptr) == EA_ERR_WORKSPACE);
-    ea_attn_desc big = desc(64, 64 * 65536, 65536);
+    ea_attn_desc big = desc(256, 256 * 65536, 65536);
     EXPECT(ea_hybrid_attn_decode_noalloc(&big, FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const uint8_t*)FAKE,
                                          FAKE, (float*)FAKE, nullptr) == EA_ERR_WORKSPACE);
     EXPECT(ea_hybrid_attn_decode_cached(&p, FAKE, FAKE, FAKE, nullptr, 10, (const int32_t*)FAKE,

@@ -351,8 +351,8 @@ def test_decode_noalloc_rejects_before_any_device_work():
     assert call(desc(num_q_heads=34, num_kv_heads=2)) == E.EA_ERR_UNSUPPORTED
     assert call(desc(head_dim=96)) == E.EA_ERR_UNSUPPORTED
     # A step whose scratch would exceed the library's array is refused:
-    # 64 sequences of 64K cached tokens need about 138 MiB of fp32 partials.
-    big = desc(num_seqs=64, total_tokens=64 * 65536, max_seqlen=65536)
+    # 256 sequences of 64K cached tokens need about 131 MiB of fp32 partials.
+    big = desc(num_seqs=256, total_tokens=256 * 65536, max_seqlen=65536)
     assert E.ea_workspace_bytes(big, E.EA_OP_DECODE) > E.EA_DECODE_NOALLOC_SCRATCH_BYTES
     assert call(big) == E.EA_ERR_WORKSPACE
     # The limit is the stated one: 8 sequences of 64K fit.

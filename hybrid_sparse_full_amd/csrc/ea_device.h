@@ -48,6 +48,42 @@ __device__ inline float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sum / max of a 32-bit value over all 64 lanes, every lane getting the
+// result, without LDS: DPP within each 16-lane row (lane ^ 1, lane ^ 2, the
+// half-row mirror, the row mirror), then v_permlane16_swap across row pairs
+// and v_permlane32_swap across the half-waves.  (The generic wave_sum below
+// goes through ds_bpermute, one LDS round trip per step.)
+template <int CTRL, typename T>
+__device__ inline T dpp_move(T v) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <typename T, typename Op>
+__device__ inline T wave_reduce_dpp(T x, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  x = op(x, dpp_move<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = op(x, dpp_move<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = op(x, dpp_move<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_move<0x140>(x));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  x = op(__builtin_bit_cast(T, (uint32_t)r[0]), __builtin_bit_cast(T, (uint32_t)r[1]));
+  const auto h = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return op(__builtin_bit_cast(T, (uint32_t)h[0]), __builtin_bit_cast(T, (uint32_t)h[1]));
+}
+__device__ inline uint32_t wave_sum_u32(uint32_t x) {
+  return wave_reduce_dpp(x, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce_dpp(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ inline float wave_sum_f32(float x) {
+  return wave_reduce_dpp(x, [](float a, float b) { return a + b; });
+}
+__device__ inline float wave_max_f32(float x) {
+  return wave_reduce_dpp(x, [](float a, float b) { return fmaxf(a, b); });
+}
+
 template <typename T>
 __device__ inline T wave_sum(T v) {
 #pragma unroll

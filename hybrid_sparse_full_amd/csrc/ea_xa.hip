@@ -393,8 +393,8 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
       zr = zr * __builtin_amdgcn_exp2f(mr - mn) + __builtin_amdgcn_exp2f(x - mn);
       mr = mn;
     }
-    const float mx = wave_max(mr);
-    const float z = wave_sum(mr == -INFINITY ? 0.f : zr * __builtin_amdgcn_exp2f(mr - mx));
+    const float mx = wave_max_f32(mr);
+    const float z = wave_sum_f32(mr == -INFINITY ? 0.f : zr * __builtin_amdgcn_exp2f(mr - mx));
     Lraw = mx + __builtin_amdgcn_logf(z);
 #pragma unroll
     for (int a = 0; a < R; ++a) La[a] = 0.f;
@@ -422,14 +422,16 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
     }
 #pragma unroll
     for (int a = 0; a < R; ++a) {
-      const float mx = wave_max(mr[a]);
-      const float z = wave_sum(mr[a] == -INFINITY ? 0.f : zr[a] * __builtin_amdgcn_exp2f(mr[a] - mx));
+      const float mx = wave_max_f32(mr[a]);
+      const float z = wave_sum_f32(mr[a] == -INFINITY ? 0.f : zr[a] * __builtin_amdgcn_exp2f(mr[a] - mx));
       La[a] = mx + __builtin_amdgcn_logf(z);
     }
   }
   // 2. Block masses P_J = (1/R) sum_a exp2(lse2[a, J] - La) and integer
-  //    weights w = max(1, floor(P * 2^24 + 1/2)).
-  uint64_t wsum = 0;
+  //    weights w = max(1, floor(P * 2^24 + 1/2)).  The masses of a row sum to
+  //    1, so every sum of weights below is at most W <= 2^24 (1 + eps) + nI,
+  //    exact in 32 bits.
+  uint32_t wsum = 0;
   uint32_t wmax = 0;
   float* bm = block_mass ? block_mass + row * d.maxqb : nullptr;
 #pragma unroll 2
@@ -456,48 +458,60 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
     wmax = w > wmax ? w : wmax;
   }
   for (int w = lane; w < d.words; w += 64) bits[w] = 0u;
-  const uint64_t W = wave_sum(wsum);
-  const uint32_t Wmax = wave_max(wmax);
+  const uint64_t W = wave_sum_u32(wsum);
+  const uint32_t Wmax = wave_max_u32(wmax);
   const uint64_t tn = (uint64_t)d.tau_num, td = (uint64_t)d.tau_den;
   const uint64_t target = tn * W;
   // 3. v* = largest v with (sum of w_J >= v) * td >= tn * W.
   uint32_t lo = 1, hi = Wmax + 1;
-  constexpr int WREG = 32;  // rows of up to 64 * WREG blocks search from registers
-  if (nI <= 64 * WREG) {
-    uint32_t wr[WREG];
+  // Rows of up to 64 * 32 blocks search from registers, NR weights per lane
+  // with NR the smallest of 4, 8, 16, 32 that holds the row.
+  auto search_regs = [&](auto nr_c) __attribute__((always_inline)) {
+    constexpr int NR = decltype(nr_c)::value;
+    uint32_t wr[NR];
 #pragma unroll
-    for (int k = 0; k < WREG; ++k) {
+    for (int k = 0; k < NR; ++k) {
       const int J = lane + 64 * k;
       const uint32_t x = wgt[J < nI ? J : 0];
       wr[k] = J < nI ? x : 0u;
     }
     while (hi - lo > 1) {
       const uint32_t mid = lo + (hi - lo) / 2;
-      uint32_t sl = 0;  // WREG weights of at most 2^24 + 1 each
+      uint32_t sl = 0;
 #pragma unroll
-      for (int k = 0; k < WREG; ++k) sl += wr[k] >= mid ? wr[k] : 0u;
-      if (wave_sum((uint64_t)sl) * td >= target) lo = mid;
+      for (int k = 0; k < NR; ++k) sl += wr[k] >= mid ? wr[k] : 0u;
+      if ((uint64_t)wave_sum_u32(sl) * td >= target) lo = mid;
       else hi = mid;
     }
+  };
+  const int nreg = (nI + 63) / 64;
+  if (nreg <= 4) {
+    search_regs(std::integral_constant<int, 4>());
+  } else if (nreg <= 8) {
+    search_regs(std::integral_constant<int, 8>());
+  } else if (nreg <= 16) {
+    search_regs(std::integral_constant<int, 16>());
+  } else if (nreg <= 32) {
+    search_regs(std::integral_constant<int, 32>());
   } else {
     while (hi - lo > 1) {
       const uint32_t mid = lo + (hi - lo) / 2;
-      uint64_t sl = 0;
+      uint32_t sl = 0;
       for (int J = lane; J < nI; J += 64) sl += wgt[J] >= mid ? wgt[J] : 0u;
-      if (wave_sum(sl) * td >= target) lo = mid;
+      if ((uint64_t)wave_sum_u32(sl) * td >= target) lo = mid;
       else hi = mid;
     }
   }
   const uint32_t vstar = lo;
-  uint64_t sg = 0;
+  uint32_t sg = 0;
   for (int J = lane; J < nI; J += 64) sg += wgt[J] > vstar ? wgt[J] : 0u;
-  const uint64_t need = target - wave_sum(sg) * td;  // > 0 by maximality of v*
+  const uint64_t need = target - (uint64_t)wave_sum_u32(sg) * td;  // > 0 by maximality of v*
   const uint64_t vt = (uint64_t)vstar * td;
   const uint64_t ceq = (need + vt - 1) / vt;  // blocks of weight v* to take, lowest J first
   // 4. Rank of each weight-v* block among equals (J order), then set bits.
   const int chunk = (nI + 63) / 64;
   const int j0 = min(nI, lane * chunk), j1 = min(nI, j0 + chunk);
-  uint64_t neq = 0;
+  uint32_t neq = 0;
   for (int J = j0; J < j1; ++J) neq += wgt[J] == vstar;
   uint64_t rank = wave_inclusive_sum(neq) - neq;
   for (int J = j0; J < j1; ++J) {
@@ -508,13 +522,13 @@ __global__ __launch_bounds__(256) void k_xa_select(EaDims d, const uint8_t* __re
     }
     if (sel) atomicOr(&bits[J >> 5], 1u << (J & 31));
   }
-  uint64_t cnt = 0;
+  uint32_t cnt = 0;
   for (int w = lane; w < d.words; w += 64) {
     const uint32_t x = bits[w];
     mrow[w] = x;
     cnt += __popc(x);
   }
-  const uint64_t count = wave_sum(cnt);
+  const uint64_t count = wave_sum_u32(cnt);
   if (lane == 0) {
     row_count[row] = (int32_t)count;
     const uint64_t pairs = (count - 1) * (uint64_t)(B * B) + (uint64_t)(B * (B + 1) / 2);

@@ -129,3 +129,18 @@ def test_decode_plan_scans_several_chunks():
                  modes=modes, ssa_sink=16, ssa_window=200, seed=9)
     assert sum(seqlens) * 8 > 256 * 2048
     _check(make_inputs(cfg), "decode 200 sequences")
+
+
+@pytest.mark.parametrize("nseq", [8, 9])
+def test_decode_plan_at_the_unit_limit(nseq):
+    # 8 KV heads of one q-head group each: 8 sequences are 64 (sequence, KV
+    # head) units, where every decode wave plans the step itself; 9 are 72,
+    # where the plan kernel does.  ~6K tokens per sequence make the device
+    # choose the split either way.
+    rng = np.random.default_rng(40 + nseq)
+    seqlens = tuple(int(x) for x in rng.integers(4000, 8000, size=nseq))
+    modes = tuple(tuple(int(m) for m in r) for r in rng.integers(0, 3, size=(nseq, 8)))
+    cfg = _small(name=f"decode-units-{nseq * 8}", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 seqlens=seqlens, modes=modes, ssa_sink=100, ssa_window=1500, seed=11)
+    assert sum(seqlens) * 8 > 2 * 64 * 2048
+    _check(make_inputs(cfg), f"decode {nseq * 8} units")

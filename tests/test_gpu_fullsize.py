@@ -6,7 +6,9 @@ oracle (computed on the host cores, head rows split over threads).
 * 64K FA-SSA layer (the benchmark's workload): every row of every q-head.
 * 64K XA-SSA layer: every mask row of all 8 XA q-heads (bit-exact outside
   boundary ties, ties counted and printed), then every row of every q-head.
-* 256K FA-XA and XA-SSA: every mask row of two XA q-heads each.
+* 256K FA-XA and XA-SSA: every mask row of two XA q-heads each, and every
+  row of two q-heads of different modes.
+* The ragged 8-sequence batch: every mask row, then every row of every q-head.
 * Configurations no other test runs: B / S = 8 and 32 at both block sizes,
   a selector row of more than 2,048 blocks, and GQA groups of 8 q-heads.
 
@@ -100,10 +102,14 @@ def test_xassa_64k_whole_layer(part):
     _check_heads(name, [(0, h) for h in range(8 * part, 8 * part + 8)], masks)
 
 
-@pytest.mark.parametrize("name,heads", [("qwen8b-faxa-256k", (4, 31)), ("qwen8b-xassa-256k", (0, 19))])
-def test_256k_every_mask_row_of_two_heads(name, heads):
+@pytest.mark.parametrize("name,heads,whole", [("qwen8b-faxa-256k", (4, 31), (0, 4)),
+                                              ("qwen8b-xassa-256k", (0, 19), (0, 4))])
+def test_256k_masks_and_whole_heads(name, heads, whole):
+    # Every mask row of two XA q-heads, then every row of two q-heads of
+    # different modes (FA-XA: FA head 0 and XA head 4; XA-SSA: XA head 0 and
+    # SSA head 4).
     inp = _inputs(name)
-    gout = PU.run_gpu(inp, block_mass=True)
+    gout = _gpu(name)
     G = inp["cfg"].gqa
     assert all(inp["modes"][0, h // G] == MODE_XA for h in heads)
     t0 = time.time()
@@ -112,6 +118,39 @@ def test_256k_every_mask_row_of_two_heads(name, heads):
     assert stats["rows"] == 2 * 2048
     print(name, f"every mask row of q-heads {heads}:", {k: v for k, v in stats.items() if k != "tie_rows"},
           f"oracle {time.time() - t0:.1f} s", flush=True)
+    wmasks = {k: v for k, v in masks.items() if k in {(0, h) for h in whole}}
+    for (b, h, I) in stats["tie_rows"]:
+        if (b, h) in wmasks:
+            M = wmasks[(b, h)][0].copy()
+            M[I, : I + 1] = PU.gpu_mask_row(gout, inp, b, h, I)
+            wmasks[(b, h)] = (M, wmasks[(b, h)][1])
+    modes = {int(inp["modes"][0, h // G]) for h in whole}
+    assert len(modes) == 2 and MODE_XA in modes
+    _check_heads(name, [(0, h) for h in whole], wmasks)
+
+
+def test_ragged_8x_whole_tensor():
+    # Every row of every q-head of the 8 ragged sequences (per-sequence modes);
+    # the XA masks first, every row, bit-exact outside boundary ties.
+    name = "ragged-8x"
+    inp = _inputs(name)
+    gout = _gpu(name)
+    cfg = inp["cfg"]
+    masks = dict(_oracle_masks(name))
+    stats = PU.check_masks(gout, inp, masks)
+    nqb = PU.qb_prefix(inp["seqlens"], cfg.block)
+    assert stats["rows"] == sum(int(nqb[b + 1] - nqb[b]) for (b, h) in masks)
+    print(name, "every mask row of", len(masks), "XA (sequence, q-head) pairs:",
+          {k: v for k, v in stats.items() if k != "tie_rows"}, flush=True)
+    for (b, h, I) in stats["tie_rows"]:
+        M = masks[(b, h)][0].copy()
+        M[I, : I + 1] = PU.gpu_mask_row(gout, inp, b, h, I)
+        masks[(b, h)] = (M, masks[(b, h)][1])
+    for b in range(len(inp["seqlens"])):
+        if int(inp["seqlens"][b]) == 0:
+            continue
+        _check_heads(name, [(b, h) for h in range(cfg.num_q_heads)],
+                     {k: v for k, v in masks.items() if k[0] == b})
 
 
 def _small(name, **kw):

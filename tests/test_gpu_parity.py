@@ -297,10 +297,6 @@ def test_xassa_64k_b64s16_sampled():
     _sampled_check("xassa-64k-b64s16", 192, 6)
 
 
-def test_ragged_8x_sampled():
-    _sampled_check("ragged-8x", 192, 5)
-
-
 def test_qwen8b_faxa_256k_sampled():
     _sampled_check("qwen8b-faxa-256k", 96, 4, xa_rows_per_head=2)
 

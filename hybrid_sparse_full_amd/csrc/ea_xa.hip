@@ -199,8 +199,9 @@ __global__ __launch_bounds__(512) void k_xa_score(EaDims d, const uint16_t* __re
       // The DMA of stage st + NS - 1 goes out between this stage's first
       // MFMAs, one instruction after every second (measured 2 % faster than
       // issuing it in one burst before them, and than one per MFMA or per
-      // three).  The DMA is what limits this loop: without it a stage runs
-      // at the MFMA rate, with it at ~60 % (its L2 misses outlast a stage).
+      // three).  The DMA is the largest single cost of the item (about a
+      // quarter of its time, growing with the bytes moved), ahead of the
+      // epilogue (about a tenth).
       const bool dnext = st + C::NS - 1 < nst;
       const int snext = st + C::NS - 1;
       constexpr int MPS = C::KSTEPS * C::NHQ * C::NA * C::NB;  // MFMAs per stage

@@ -461,8 +461,8 @@ def main():
                           "FA + SSA (sink 128, window 2048), seeded N(0,1) on the device"}), flush=True)
         return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
-                                   "design note, not an implemented path", "n_gpus": a.gpus}))
+        print(json.dumps({"error": "the library runs on one GPU only; sharding over several GPUs is "
+                                   "described, not implemented", "n_gpus": a.gpus}))
         sys.exit(2)
     import torch
     from hybrid_sparse_full_amd.layer import HybridPrefill, bf16_tensor, desc_for

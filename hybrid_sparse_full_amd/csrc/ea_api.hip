@@ -16,6 +16,7 @@ static ea_status make_dims(const ea_attn_desc* desc, EaDims* d) {
     return EA_ERR_INVALID_ARG;
   if (a.num_seqs == 0 && a.total_tokens != 0) return EA_ERR_INVALID_ARG;
   if (a.max_seqlen > a.total_tokens) return EA_ERR_INVALID_ARG;
+  if (a.total_tokens > EA_MAX_TOKENS) return EA_ERR_UNSUPPORTED;  // 32-bit token indices in the kernels
   // A valid cu_seqlens needs max_seqlen * num_seqs >= total_tokens.
   if ((int64_t)a.max_seqlen * a.num_seqs < (int64_t)a.total_tokens) return EA_ERR_INVALID_ARG;
   if (!(a.softmax_scale > 0.0f) || !std::isfinite(a.softmax_scale)) return EA_ERR_INVALID_ARG;

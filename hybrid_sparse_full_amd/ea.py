@@ -39,6 +39,7 @@ EXPORTS = (
 
 # Size of the library-owned scratch of ea_hybrid_attn_decode_noalloc.
 EA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+EA_MAX_TOKENS = 0x7FFF0000
 
 # Router weight arrays in ea_router_desc order: Task MLP (w1, b1, w2, b2),
 # Router MLP (w3, b3, w4, b4); fp32, row-major [in][out].

@@ -57,9 +57,16 @@ typedef enum {
 
 typedef enum { EA_MODE_FA = 0, EA_MODE_SSA = 1, EA_MODE_XA = 2 } ea_mode;
 
+/* Largest total_tokens (and so max_seqlen) the kernels accept: 2^31 - 2^16.
+ * Token indices are 32-bit inside the kernels; the headroom keeps a token
+ * index plus a tile's or a decode split's offset (at most 4,096) below 2^31.
+ * A larger descriptor gets EA_ERR_UNSUPPORTED from every call that takes
+ * one, and ea_workspace_bytes returns 0 for it. */
+#define EA_MAX_TOKENS 0x7fff0000
+
 typedef struct {
   int32_t num_seqs;      /* >= 0 */
-  int32_t total_tokens;  /* T = cu_seqlens[num_seqs], >= 0 */
+  int32_t total_tokens;  /* T = cu_seqlens[num_seqs], 0 <= T <= EA_MAX_TOKENS */
   int32_t max_seqlen;    /* upper bound of every sequence length */
   int32_t num_q_heads;   /* Hq >= 1 */
   int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */

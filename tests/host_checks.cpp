@@ -48,8 +48,8 @@ static ea_attn_desc desc(int nseq, int T, int maxL, int hq = 32, int hkv = 8, in
 static void* const FAKE = reinterpret_cast<void*>(uintptr_t{0x10000});
 
 int main() {
-  // 1. Sizing over a grid of descriptors, up to 2^31 - 1 tokens.
-  const int lens[] = {0, 1, 127, 128, 129, 65536, 262144, 1 << 30, 2147483647};
+  // 1. Sizing over a grid of descriptors, up to the largest accepted batch.
+  const int lens[] = {0, 1, 127, 128, 129, 65536, 262144, 1 << 30, EA_MAX_TOKENS};
   for (int L : lens)
     for (int nseq : {1, 2, 7}) {
       for (int hkv : {1, 8, 64}) {
@@ -63,6 +63,11 @@ int main() {
         EXPECT(ea_mask_words(&a) >= 0);
       }
     }
+  for (int nseq : {1, 2}) {
+    // One token past the limit: no size for any operation.
+    ea_attn_desc over = desc(nseq, EA_MAX_TOKENS + 1, EA_MAX_TOKENS + 1);
+    for (int op = 0; op <= 3; ++op) EXPECT(ea_workspace_bytes(&over, op) == 0);
+  }
   ea_attn_desc bad = desc(1, 100, 100);
   bad.head_dim = 96;
   EXPECT(ea_workspace_bytes(&bad, EA_OP_PREFILL) == 0);

@@ -317,9 +317,10 @@ def test_decode_rejects_bad_arguments_and_sizes_workspace():
 
 
 def test_workspace_sizes_do_not_wrap_near_int32_max():
-    # 2^31 - 1 tokens in one or two sequences, a sink as long as the cache:
-    # every size is an honest upper bound (no int32 wrap in ceil-divisions).
-    T = 2 ** 31 - 1
+    # The largest accepted batch (2^31 - 2^16 tokens) in one or two sequences,
+    # a sink as long as the cache: every size is an honest upper bound (no
+    # int32 wrap in ceil-divisions).
+    T = E.EA_MAX_TOKENS
     for kw in (dict(num_seqs=2, num_q_heads=8, num_kv_heads=8),
                dict(num_seqs=1, num_q_heads=32, num_kv_heads=8, ssa_sink=T)):
         d = desc(total_tokens=T, max_seqlen=T, **kw)
@@ -330,6 +331,50 @@ def test_workspace_sizes_do_not_wrap_near_int32_max():
         # fp32 partials of splits of at least 512 keys, per (sequence, q-head)
         assert 4 * hq * (T // 4096) * 130 <= dec < 2 ** 40
         assert 0 < E.ea_workspace_bytes(d, E.EA_OP_XA_SELECT) < 2 ** 60
+
+
+def test_token_limit_is_enforced_by_every_call():
+    # One token past EA_MAX_TOKENS: every call that takes a descriptor
+    # rejects it on the host, before touching a pointer.
+    src = open(os.path.join(ROOT, "include", "ea.h")).read()
+    m = re.search(r"#define EA_MAX_TOKENS (0x[0-9a-fA-F]+)", src)
+    assert m and int(m.group(1), 16) == E.EA_MAX_TOKENS == 2 ** 31 - 2 ** 16
+    lib = E.lib()
+    ok = desc(total_tokens=E.EA_MAX_TOKENS, max_seqlen=E.EA_MAX_TOKENS, num_seqs=1)
+    big = desc(total_tokens=E.EA_MAX_TOKENS + 1, max_seqlen=E.EA_MAX_TOKENS + 1, num_seqs=1)
+    for op in (E.EA_OP_XA_SELECT, E.EA_OP_PREFILL, E.EA_OP_DECODE):
+        assert E.ea_workspace_bytes(ok, op) > 0
+        assert E.ea_workspace_bytes(big, op) == 0
+    W = 1 << 62
+    assert lib.ea_hybrid_attn_prefill(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                      FAKE, W, None) == E.EA_ERR_UNSUPPORTED
+    assert lib.ea_xa_block_select(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                  FAKE, W, None) == E.EA_ERR_UNSUPPORTED
+    assert lib.ea_hybrid_attn_plan(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None, FAKE, W,
+                                   None) == E.EA_ERR_UNSUPPORTED
+    assert lib.ea_hybrid_attn_run(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, W,
+                                  None) == E.EA_ERR_UNSUPPORTED
+    assert lib.ea_hybrid_attn_decode(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, W,
+                                     None) == E.EA_ERR_UNSUPPORTED
+    assert lib.ea_hybrid_attn_decode_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                             None) == E.EA_ERR_UNSUPPORTED
+    modes = np.zeros(8, dtype=np.uint8)
+    assert lib.ea_hybrid_attn_prefill_serial(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, modes.ctypes.data,
+                                             FAKE, FAKE, FAKE, W, None) == E.EA_ERR_UNSUPPORTED
+    assert lib.ea_route_heads(ctypes.byref(big), ctypes.byref(_router_desc()), FAKE, FAKE, MODE_FA, MODE_SSA,
+                              FAKE, FAKE, None) == E.EA_ERR_UNSUPPORTED
+    for fn in (lib.ea_decode_cache_fill, lib.ea_decode_cache_append):
+        assert fn(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, None) == E.EA_ERR_UNSUPPORTED
+    assert lib.ea_hybrid_attn_decode_cached(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, W, None) == E.EA_ERR_UNSUPPORTED
+    seg = np.zeros(9, dtype=np.int64)
+    assert lib.ea_decode_cache_layout(ctypes.byref(big), modes.ctypes.data,
+                                      np.array([1], dtype=np.int32).ctypes.data,
+                                      seg.ctypes.data) == E.EA_ERR_UNSUPPORTED
+    cu = np.array([0, E.EA_MAX_TOKENS + 1], dtype=np.int32)
+    out = [np.zeros(2), np.zeros(2), np.zeros(8), np.zeros(1)]
+    assert lib.ea_sparsity_ratios(ctypes.byref(big), cu.ctypes.data, modes.ctypes.data, MODE_SSA, None,
+                                  *[x.ctypes.data for x in out]) == E.EA_ERR_UNSUPPORTED
 
 
 def test_decode_noalloc_rejects_before_any_device_work():

@@ -102,7 +102,7 @@ __device__ inline int32_t dec_key(int mode, int32_t p, int32_t L, int32_t sink, 
 
 __device__ inline void seq_bounds(const DecArgs& a, int b, int32_t* s0, int32_t* L) {
   const int32_t s = min(max(a.cu[b], 0), a.T);
-  const int32_t e = min(min(max(a.cu[b + 1], s), a.T), s + a.maxL);
+  const int32_t e = (int32_t)min<int64_t>(min(max(a.cu[b + 1], s), a.T), (int64_t)s + a.maxL);
   *s0 = s;
   *L = e - s;
 }

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(ROUTER_NT) void k_route(RouterArgs a) {
 
   // Sequence bounds, clamped into [0, T) with the length capped at maxL.
   const int32_t s0 = min(max(a.cu[b], 0), a.T);
-  const int32_t e0 = min(min(max(a.cu[b + 1], s0), a.T), s0 + a.maxL);
+  const int32_t e0 = (int32_t)min<int64_t>(min(max(a.cu[b + 1], s0), a.T), (int64_t)s0 + a.maxL);
   const int32_t L = e0 - s0;
   // Boundary set: local tokens [0, h0) and [t0, L), t0 >= h0, each once.
   const int32_t h0 = min(a.w.pool_head, L);

@@ -187,10 +187,26 @@ __global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
   int32_t* cur = in_lds ? lcur : cursor;
   const int tid = threadIdx.x;
   const int32_t nb = d.maxqb + 1;  // costs 0..maxqb
+  const int32_t nu = m.scal[SCAL_N_UNITS];
+  const int64_t nr = (int64_t)nu * d.ngr;
+  const int64_t chunk = (nr + SCHED_NT - 1) / SCHED_NT;
+  const int64_t r0 = min(nr, tid * chunk), r1 = min(nr, r0 + chunk);
+  // Every cost load goes out first, so that their latency overlaps the
+  // bucket scan: UPT unit costs and RPT row costs per thread in registers
+  // (the rest, on larger batches, loaded where they are used).
+  constexpr int UPT = 8, RPT = 16;
+  int32_t uc[UPT], rc[RPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int32_t u = tid + i * SCHED_NT;
+    uc[i] = u < nu ? unit_cost[u] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) rc[i] = r0 + i < r1 ? row_cost[r0 + i] : 0;
   // Bucket starts in descending cost order: cursor[c] = sum_{c' > c} hist[c'].
   {
-    const int chunk = (nb + SCHED_NT - 1) / SCHED_NT;
-    const int i0 = min(nb, tid * chunk), i1 = min(nb, i0 + chunk);
+    const int bchunk = (nb + SCHED_NT - 1) / SCHED_NT;
+    const int i0 = min(nb, tid * bchunk), i1 = min(nb, i0 + bchunk);
     int64_t s = 0;
     for (int i = i0; i < i1; ++i) s += hist[d.maxqb - i];
     int64_t tot;
@@ -201,20 +217,28 @@ __global__ __launch_bounds__(SCHED_NT) void k_sched(EaDims d, SeqMeta m,
     }
   }
   __syncthreads();
-  const int32_t nu = m.scal[SCAL_N_UNITS];
-  for (int32_t u = tid; u < nu; u += SCHED_NT) {
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int32_t u = tid + i * SCHED_NT;
+    if (u < nu) sorted_units[atomicAdd(&cur[uc[i]], 1)] = u;
+  }
+  for (int32_t u = tid + UPT * SCHED_NT; u < nu; u += SCHED_NT) {
     const int32_t pos = atomicAdd(&cur[unit_cost[u]], 1);
     sorted_units[pos] = u;
   }
   // Row offsets into the flat tile list (natural row order).
-  const int64_t nr = (int64_t)nu * d.ngr;
-  const int64_t chunk = (nr + SCHED_NT - 1) / SCHED_NT;
-  const int64_t r0 = min(nr, tid * chunk), r1 = min(nr, r0 + chunk);
   int64_t s = 0;
-  for (int64_t r = r0; r < r1; ++r) s += row_cost[r];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) s += rc[i];
+  for (int64_t r = r0 + RPT; r < r1; ++r) s += row_cost[r];
   int64_t tot;
   int64_t e = block_exclusive_sum<SCHED_NT>(s, sm, &tot);
-  for (int64_t r = r0; r < r1; ++r) {
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    if (r0 + i < r1) row_off[r0 + i] = e;
+    e += rc[i];
+  }
+  for (int64_t r = r0 + RPT; r < r1; ++r) {
     row_off[r] = e;
     e += row_cost[r];
   }

@@ -135,17 +135,27 @@ __global__ __launch_bounds__(256) void k_cost(EaDims d, const uint8_t* __restric
     } else if (ri.mode == EA_MODE_XA) {
       // Union of the blocks selected by the heads of this group.
       const uint32_t* row = xa_mask + ((int64_t)qbg * d.Hq + g * d.G + kg * d.hpw) * d.words;
+      // Words 0 .. I / 32 hold the blocks J <= I; 8 words of both heads
+      // (hpw <= 2) are loaded before any is used.
       c = 0;
-      for (int w = 0; w * 32 <= ri.I; ++w) {
-        const int hi = ri.I - w * 32;  // keep J <= I
-        const uint32_t keep = hi < 31 ? (2u << hi) - 1u : 0xffffffffu;
-        uint32_t bits = 0;
-        for (int e = 0; e < d.hpw; ++e) {
-          const uint32_t be = row[(int64_t)e * d.words + w] & keep;
-          head_tiles += __popc(be);
-          bits |= be;
+      const int nw = ri.I / 32 + 1;
+      const uint32_t* row1 = row + (d.hpw > 1 ? d.words : 0);
+      for (int w0 = 0; w0 < nw; w0 += 8) {
+        uint32_t b0[8], b1[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bool in = w0 + t < nw;
+          b0[t] = in ? row[w0 + t] : 0u;
+          b1[t] = in && d.hpw > 1 ? row1[w0 + t] : 0u;
         }
-        c += __popc(bits);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int hi = ri.I - (w0 + t) * 32;  // keep J <= I
+          const uint32_t keep = hi < 0 ? 0u : hi < 31 ? (2u << hi) - 1u : 0xffffffffu;
+          const uint32_t a0 = b0[t] & keep, a1 = b1[t] & keep;
+          head_tiles += __popc(a0) + __popc(a1);
+          c += __popc(a0 | a1);
+        }
       }
     } else {
       c = ri.I + 1;

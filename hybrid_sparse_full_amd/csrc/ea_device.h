@@ -91,16 +91,6 @@ __device__ inline T wave_sum(T v) {
   return v;
 }
 
-template <typename T>
-__device__ inline T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T u = __shfl_xor(v, o, 64);
-    v = u > v ? u : v;
-  }
-  return v;
-}
-
 // Block-wide exclusive prefix sum for blocks of NT threads (NT % 64 == 0).
 // `smem` needs NT / 64 + 1 elements.  Returns the exclusive prefix of the
 // calling thread; *total receives the block sum.  Contains barriers: every
@@ -157,13 +147,6 @@ __device__ inline T block_exclusive_max(T v, T lo, T* smem) {
   T res = smem[w] > exc ? smem[w] : exc;
   __syncthreads();
   return res;
-}
-
-template <int NT, typename T>
-__device__ inline T block_sum(T v, T* smem) {
-  T tot;
-  block_exclusive_sum<NT, T>(v, smem, &tot);
-  return tot;
 }
 
 // Largest index p in [0, n) with a[p] <= x, for nondecreasing a with a[0] <= x.

@@ -567,9 +567,10 @@ ea_status ea_hybrid_attn_decode_noalloc(const ea_attn_desc* desc, const void* q_
   void* ws = nullptr;
   st = scratch_of_current_device(&ws);
   if (st != EA_OK) return st;
-  // Nothing in the scratch has to start at zero: the plan kernel writes the
-  // split and the wave list, and the combine reads only the partials that
-  // this step's own waves wrote.
+  // Nothing in the scratch has to start at zero: the split is written by
+  // k_decode_plan (with the workgroup list) or, for steps of at most 64
+  // units, by the first k_decode workgroup, and the combine reads only the
+  // partials that this step's own workgroups wrote.
   if (launch_decode(d, (const uint16_t*)q_dev, (const uint16_t*)k_dev, (const uint16_t*)v_dev,
                     cu_seqlens_dev, modes_dev, ws, L, (uint16_t*)o_out_dev, lse_out_dev,
                     (hipStream_t)stream) != hipSuccess)

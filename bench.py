@@ -523,6 +523,29 @@ def main():
     _, router_ms, _ = time_steps(lambda: router(desc, k, layer.cu, 0, cfg.sparse_mode, routed),
                                  max(a.steps, 20), a.warmup)
 
+    # End to end with routing on the device: the router writes the modes into
+    # device memory, XA selection (when the mode set has XA) and the prefill
+    # read them there, with no host round trip.  The retrieval mode of the
+    # set is the workload's most common mode other than its sparse mode.  The
+    # random weights choose their own modes, so the same layer with those
+    # modes passed in is timed beside it.
+    other = inp["modes"][inp["modes"] != cfg.sparse_mode]
+    rmode = int(np.bincount(other, minlength=3).argmax()) if other.size else 0
+    rlayer = HybridPrefill(desc, inp["cu_seqlens"], None, device=dev, mode_set=(rmode, cfg.sparse_mode))
+    _, routed_ms, _ = time_steps(lambda: (rlayer.route(router, k), rlayer(q, k, v)), a.steps, a.warmup)
+    rmodes = rlayer.device_modes()
+    del rlayer
+    plain = HybridPrefill(desc, inp["cu_seqlens"], rmodes, device=dev)
+    _, plain_ms, _ = time_steps(lambda: plain(q, k, v), a.steps, a.warmup)
+    del plain
+    routed_layer = {
+        "ms_per_layer": round(routed_ms, 4),
+        "same_modes_passed_in_ms": round(plain_ms, 4),
+        "mode_set": [rmode, int(cfg.sparse_mode)],
+        "modes_chosen": np.bincount(rmodes.reshape(-1), minlength=3).tolist(),
+        "weights": "seeded random (no trained router weights)",
+    }
+
     decode = None
     if a.decode_batch > 0:
         decode = decode_bench(cfg, inp["modes"][0], int(np.max(inp["seqlens"])), a.decode_batch,
@@ -599,6 +622,7 @@ def main():
             "hidden": 4 * D,
             "weights": "seeded random (no trained router weights)",
         },
+        "routed_layer": routed_layer,
         "roofline": {
             "kernel": "k_attn (fused hybrid attention)",
             "bound": "mfma",

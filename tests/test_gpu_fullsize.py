@@ -9,6 +9,10 @@ oracle (computed on the host cores, head rows split over threads).
 * 256K FA-XA and XA-SSA: every mask row of two XA q-heads each, and every
   row of two q-heads of different modes.
 * The ragged 8-sequence batch: every mask row, then every row of every q-head.
+* The XA variants at 64K (Table 8's block 64 / stride 16, one mask per KV
+  head, block-sum masses): every mask row of all 8 XA q-heads (of one q-head
+  per XA KV head for the block-sum masses), then every row of one XA and one
+  SSA q-head.
 * Configurations no other test runs: B / S = 8 and 32 at both block sizes,
   a selector row of more than 2,048 blocks, and GQA groups of 8 q-heads.
 
@@ -127,6 +131,30 @@ def test_256k_masks_and_whole_heads(name, heads, whole):
     modes = {int(inp["modes"][0, h // G]) for h in whole}
     assert len(modes) == 2 and MODE_XA in modes
     _check_heads(name, [(0, h) for h in whole], wmasks)
+
+
+@pytest.mark.parametrize("name", ["xassa-64k-b64s16", "xassa-64k-group", "xassa-64k-r1"])
+def test_xa_variants_every_mask_row_and_whole_heads(name):
+    inp = _inputs(name)
+    gout = _gpu(name)
+    cfg = inp["cfg"]
+    t0 = time.time()
+    # The block-sum oracle sums every antidiagonal entry in explicit loops
+    # (~12 s per head at 64K): one q-head per XA KV head there, all 8 else.
+    heads = {(0, 0), (0, 16)} if cfg.xa_norm else None
+    masks = dict(PU.oracle_xa_parallel(inp, heads) if heads else _oracle_masks(name))
+    stats = PU.check_masks(gout, inp, masks)
+    n = len(heads) if heads else 8
+    assert len(masks) == n and stats["rows"] == n * (int(inp["seqlens"][0]) // cfg.block)
+    print(name, f"every mask row of {n} XA q-heads:", {k: v for k, v in stats.items() if k != "tie_rows"},
+          f"oracle {time.time() - t0:.1f} s", flush=True)
+    for (b, h, I) in stats["tie_rows"]:
+        M = masks[(b, h)][0].copy()
+        M[I, : I + 1] = PU.gpu_mask_row(gout, inp, b, h, I)
+        masks[(b, h)] = (M, masks[(b, h)][1])
+    G = cfg.gqa
+    assert inp["modes"][0, 0] == MODE_XA and inp["modes"][0, 4 // G] == MODE_SSA
+    _check_heads(name, [(0, 0), (0, 4)], {k: v for k, v in masks.items() if k == (0, 0)})
 
 
 def test_ragged_8x_whole_tensor():

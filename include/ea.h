@@ -134,6 +134,10 @@ int32_t ea_mask_words(const ea_attn_desc* desc);
  * selected, which is what tau = 1 selects and makes XA equal to FA
  * (row_count = I + 1 on every such row).
  *
+ * A row's masses and weights are held in LDS, so max_seqlen may span at most
+ * 12,288 blocks (1,572,864 tokens at B = 128); a longer descriptor gets
+ * EA_ERR_UNSUPPORTED.
+ *
  * Inputs  q [T,Hq,d] bf16, k [T,Hkv,d] bf16, cu_seqlens_dev int32[num_seqs+1],
  *         modes_dev uint8[num_seqs * Hkv] (row-major [seq][kv head]).
  * Outputs (device; all ea_mask_rows rows are written)

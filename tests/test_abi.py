@@ -333,6 +333,16 @@ def test_workspace_sizes_do_not_wrap_near_int32_max():
         assert 0 < E.ea_workspace_bytes(d, E.EA_OP_XA_SELECT) < 2 ** 60
 
 
+def test_select_rejects_rows_longer_than_12288_blocks():
+    # The selector holds a block row in LDS: 12,288 blocks at most.
+    lib = E.lib()
+    for nb, code in ((12288, E.EA_ERR_WORKSPACE), (12289, E.EA_ERR_UNSUPPORTED)):
+        d = desc(total_tokens=nb * 128, max_seqlen=nb * 128, num_seqs=1)
+        st = lib.ea_xa_block_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                    0, None)
+        assert st == code, (nb, st)
+
+
 def test_token_limit_is_enforced_by_every_call():
     # One token past EA_MAX_TOKENS: every call that takes a descriptor
     # rejects it on the host, before touching a pointer.

@@ -13,6 +13,9 @@ oracle (computed on the host cores, head rows split over threads).
   head, block-sum masses): every mask row of all 8 XA q-heads (of one q-head
   per XA KV head for the block-sum masses), then every row of one XA and one
   SSA q-head.
+* One sequence of 2^20 tokens (q holds 2^32 elements): query rows at both
+  ends and the middle of an FA and an SSA q-head, and a decode step over the
+  same cache against the prefill's last row.
 * Configurations no other test runs: B / S = 8 and 32 at both block sizes,
   a selector row of more than 2,048 blocks, and GQA groups of 8 q-heads.
 
@@ -243,3 +246,57 @@ def test_gqa_group_of_8(D, B):
     cfg = _small(f"gqa8-D{D}-B{B}", num_q_heads=64, num_kv_heads=8, head_dim=D, block=B,
                  xa_stride=B // 16, seqlens=(8 * B, 5 * B + 11), modes=modes)
     _full(make_inputs(cfg), f"GQA 8 D{D} B{B}")
+
+
+def test_one_million_token_sequence():
+    # 2^20 tokens, Llama-3.1-8B shape, KV head 0 FA and the rest SSA: q and o
+    # hold 2^32 elements, so element offsets past 2^32 are exercised.  Inputs
+    # are drawn on the device; the oracle gets the rows it needs.
+    import torch
+    from hybrid_sparse_full_amd.layer import HybridDecode, HybridPrefill, make_desc
+    from oracle import attention as OA
+    dev = torch.device("cuda:0")
+    L, Hq, Hkv, D, B, sink, window = 1 << 20, 32, 8, 128, 128, 128, 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20)
+    q = torch.randn((L, Hq, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    k = torch.randn((L, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    v = torch.randn((L, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    modes = np.array([[MODE_FA] + [MODE_SSA] * (Hkv - 1)], dtype=np.uint8)
+    cu = np.array([0, L], dtype=np.int32)
+    desc = make_desc(num_seqs=1, total_tokens=L, max_seqlen=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                     block=B, ssa_sink=sink, ssa_window=window)
+    layer = HybridPrefill(desc, cu, modes, device=dev)
+    t0 = time.time()
+    layer(q, k, v)
+    torch.cuda.synchronize()
+    print(f"1M prefill {time.time() - t0:.2f} s", flush=True)
+    scale = desc.softmax_scale
+    qi = [0, 1, B - 1, B, L // 2 + 77, L - B - 1, L - B, L - 1]
+    for h in (1, 9):  # FA (KV head 0) and SSA (KV head 2)
+        g = h // (Hq // Hkv)
+        kg = k[:, g].double().cpu().numpy()
+        vg = v[:, g].double().cpu().numpy()
+        o_ref, l_ref = [], []
+        for i in qi:
+            o_i, l_i = OA.row_attention(q[i, h].double().cpu().numpy(), kg, vg, i, int(modes[0, g]), scale,
+                                        sink=sink, window=window, block=B)
+            o_ref.append(o_i)
+            l_ref.append(l_i)
+        idx = torch.tensor(qi, device=dev)
+        o = layer.o[idx, h].double().cpu().numpy()
+        lse = layer.lse[h, idx].double().cpu().numpy()
+        print(f"1M head {h}", PU.check_close(o, np.array(o_ref), lse, np.array(l_ref), f"1M head {h}"), flush=True)
+        del kg, vg
+    # One decode step whose query is the last token's: the prefill's last row.
+    o_last = layer.o[L - 1].clone()
+    lse_last = layer.lse[:, L - 1].clone()
+    del layer
+    dec = HybridDecode(desc, cu, modes, device=dev)
+    dec(q[L - 1:L].contiguous(), k, v)
+    torch.cuda.synchronize()
+    d_o = dec.o[0].double().cpu().numpy()
+    d_l = dec.lse[0].double().cpu().numpy()
+    print("1M decode vs prefill last row",
+          PU.check_close(d_o, o_last.double().cpu().numpy(), d_l, lse_last.double().cpu().numpy(), "1M decode"),
+          flush=True)

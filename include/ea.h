@@ -341,6 +341,8 @@ ea_status ea_decode_cache_fill(const ea_attn_desc* desc, const void* k_dev, cons
  * are written as key L_b - 1 of each segment, where cu_seqlens_dev gives the
  * lengths L_b after the append (an empty sequence appends nothing).  An SSA
  * ring overwrites the slot of the key that just left the window.
+ * As for ea_hybrid_attn_decode_cached, desc.total_tokens and max_seqlen may
+ * be upper bounds of the lengths.
  */
 ea_status ea_decode_cache_append(const ea_attn_desc* desc, const void* k_new_dev,
                                  const void* v_new_dev, const int32_t* cu_seqlens_dev,
@@ -352,9 +354,14 @@ ea_status ea_decode_cache_append(const ea_attn_desc* desc, const void* k_new_dev
  * One decode step over the segmented cache: the same step, split plan and
  * key order as ea_hybrid_attn_decode over the packed cache that holds the
  * same keys, so the outputs are bit-identical.  cu_seqlens_dev gives the
- * cached lengths L_b (desc.total_tokens = their sum; the current token is
- * cached); q, o, lse, modes, workspace (EA_OP_DECODE) and limits as for
- * ea_hybrid_attn_decode.
+ * cached lengths L_b (the current token is cached); q, o, lse, modes,
+ * workspace (EA_OP_DECODE) and limits as for ea_hybrid_attn_decode.
+ * desc.total_tokens and desc.max_seqlen may be upper bounds of the sum and
+ * the longest of the L_b (for example the capacity the layout was built
+ * for): then one descriptor, one workspace and one captured graph serve
+ * every step of a decode loop whose lengths grow in cu_seqlens_dev.  (The
+ * split, and so the rounding, follows the descriptor: equal descriptors give
+ * bit-identical results.)
  */
 ea_status ea_hybrid_attn_decode_cached(const ea_attn_desc* desc, const void* q_dev,
                                        const void* k_cache_dev, const void* v_cache_dev,

@@ -207,3 +207,80 @@ def test_decode_graph_replays_match_eager():
     assert np.all(o[~keep] == 0) and np.all(np.isneginf(lse[~keep]))
     print(PU.check_close(o[keep].reshape(-1), O[keep].reshape(-1), lse[keep], LSE[keep], "decode graph replay"),
           flush=True)
+
+
+def test_segmented_cache_decode_loop_graph():
+    # A serving loop: every step appends one token per sequence to the
+    # segmented cache and decodes it.  The descriptor holds the capacity (an
+    # upper bound of the lengths), so one capture serves every step; between
+    # replays only device buffers change: the lengths and the new k, v and q.
+    # A twin cache driven by eager calls must match every replay bit for bit,
+    # and the last step matches the oracle over each sequence's whole history.
+    from hybrid_sparse_full_amd.layer import SegmentedDecodeCache
+    nseq, Hq, Hkv, D, sink, window, steps = 3, 8, 2, 128, 16, 64, 6
+    L0 = np.array([100, 37, 200])
+    cap = L0 + steps
+    modes = np.array([[MODE_FA, MODE_SSA], [MODE_SSA, MODE_XA], [MODE_SSA, MODE_SSA]], dtype=np.uint8)
+    desc = make_desc(num_seqs=nseq, total_tokens=int(cap.sum()), max_seqlen=int(cap.max()), num_q_heads=Hq,
+                     num_kv_heads=Hkv, head_dim=D, block=128, ssa_sink=sink, ssa_window=window)
+    desc0 = make_desc(num_seqs=nseq, total_tokens=int(L0.sum()), max_seqlen=int(L0.max()), num_q_heads=Hq,
+                      num_kv_heads=Hkv, head_dim=D, block=128, ssa_sink=sink, ssa_window=window)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(51)
+    kh = [torch.randn((int(c), Hkv, D), generator=gen, device=DEV).to(torch.bfloat16) for c in cap]
+    vh = [torch.randn((int(c), Hkv, D), generator=gen, device=DEV).to(torch.bfloat16) for c in cap]
+    qs = torch.randn((steps, nseq, Hq, D), generator=gen, device=DEV).to(torch.bfloat16)
+
+    def cu_of(lens):
+        return torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+
+    k0 = torch.cat([kh[b][:L0[b]] for b in range(nseq)])
+    v0 = torch.cat([vh[b][:L0[b]] for b in range(nseq)])
+    caches = [SegmentedDecodeCache(desc, modes, cap.astype(np.int32), device=DEV) for _ in range(2)]
+    for c in caches:
+        c.fill(desc0, k0, v0, cu_of(L0))
+    ws = [torch.empty(E.ea_workspace_bytes(desc, E.EA_OP_DECODE), dtype=torch.uint8, device=DEV) for _ in range(2)]
+    outs = [(torch.empty((nseq, Hq, D), dtype=torch.bfloat16, device=DEV),
+             torch.empty((nseq, Hq), dtype=torch.float32, device=DEV)) for _ in range(2)]
+    cu = torch.empty(nseq + 1, dtype=torch.int32, device=DEV)
+    k_new = torch.empty((nseq, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    v_new = torch.empty_like(k_new)
+    q = torch.empty((nseq, Hq, D), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        c, (o, lse) = caches[i], outs[i]
+        c.append(desc, k_new, v_new, cu)
+        c.decode(desc, q, cu, o, lse, ws[i])
+
+    def set_inputs(s):
+        lens = L0 + s + 1
+        cu.copy_(cu_of(lens))
+        for b in range(nseq):
+            k_new[b].copy_(kh[b][lens[b] - 1])
+            v_new[b].copy_(vh[b][lens[b] - 1])
+        q.copy_(qs[s])
+        torch.cuda.synchronize()
+        return lens
+
+    g = None
+    for s in range(steps):
+        lens = set_inputs(s)
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(0)
+            torch.cuda.synchronize()
+        _garble(list(outs[0]))
+        g.replay()
+        step(1)
+        torch.cuda.synchronize()
+        for a, b in zip(outs[0], outs[1]):
+            assert torch.equal(_bits(a), _bits(b)), f"step {s}: the replay differs from the eager loop"
+        print(f"cache loop step {s} (lengths {lens.tolist()}) replay equals eager", flush=True)
+    kp = torch.cat([kh[b][:lens[b]] for b in range(nseq)]).double().cpu().numpy()
+    vp = torch.cat([vh[b][:lens[b]] for b in range(nseq)]).double().cpu().numpy()
+    O, LSE = OD.decode(qs[steps - 1].double().cpu().numpy(), kp, vp,
+                       np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), modes,
+                       scale=desc.softmax_scale, sink=sink, window=window)
+    print(PU.check_close(outs[0][0].double().cpu().numpy().reshape(-1), O.reshape(-1),
+                         outs[0][1].double().cpu().numpy(), LSE, "cache loop, last step"), flush=True)

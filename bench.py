@@ -284,8 +284,9 @@ def cpu_baseline(inp, seconds, threads=None):
 
 
 def oracle_timing(names, threads):
-    """Wall time of the whole fp64 oracle layer (every row of every FA / SSA
-    q-head) per workload, with `threads` host threads."""
+    """The CPU baseline over whole layers: wall time of the fp64 oracle layer
+    (every row of every FA / SSA q-head) per workload, with `threads` host
+    threads.  Like cpu_baseline, it times the oracle and runs no GPU work."""
     from synth import get_config, make_inputs
     out = []
     for name in names:

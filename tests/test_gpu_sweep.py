@@ -6,8 +6,9 @@ tau, SSA sink and window (including 0 / 1 and longer than the sequences),
 needle layout, ragged lengths around block edges (empty and one-token
 sequences included) and random modes per (sequence, KV head).  Prefill with
 XA selection must match the oracle (masks bit-exact outside boundary ties,
-O and LSE within the tolerances), and a decode step over the same cache must
-match the decode oracle.  Small enough that the oracle runs whole tensors.
+O and LSE within the tolerances), a decode step over the same cache must
+match the decode oracle, and the segmented cache filled from it must decode
+bit for bit the same.  Small enough that the oracle runs whole tensors.
 """
 
 import numpy as np
@@ -15,7 +16,7 @@ import pytest
 import torch
 
 from hybrid_sparse_full_amd import ea as E
-from hybrid_sparse_full_amd.layer import HybridDecode, bf16_tensor, desc_for
+from hybrid_sparse_full_amd.layer import HybridDecode, SegmentedDecodeCache, bf16_tensor, desc_for
 from oracle import decode as OD
 from synth import get_config, make_inputs, bf16_bits_to_f64
 import parity_utils as PU
@@ -86,3 +87,14 @@ def test_parameter_sweep(seed):
     assert np.all(o[~keep] == 0) and np.all(np.isneginf(lse[~keep])), tag
     print("  decode", PU.check_close(o[keep].reshape(-1), Od[keep].reshape(-1), lse[keep], Ld[keep], tag),
           flush=True)
+
+    # The segmented cache (SSA heads keep sink + window keys), filled from the
+    # same keys, decodes bit for bit like the packed cache.
+    cache = SegmentedDecodeCache(d, inp["modes"], np.asarray(inp["seqlens"], dtype=np.int32), device=DEV)
+    cu_dev = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).to(DEV)
+    cache.fill(d, bf16_tensor(inp["k"], DEV), bf16_tensor(inp["v"], DEV), cu_dev)
+    oc, lc = torch.empty_like(dec.o), torch.empty_like(dec.lse)
+    cache.decode(d, bf16_tensor(qn, DEV), cu_dev, oc, lc, torch.empty_like(dec.ws))
+    torch.cuda.synchronize()
+    assert torch.equal(oc.view(torch.int16), dec.o.view(torch.int16)), tag
+    assert torch.equal(lc.view(torch.int32), dec.lse.view(torch.int32)), tag
